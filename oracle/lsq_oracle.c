@@ -1,0 +1,350 @@
+/*
+ * CPU oracle for the low-bit recurrent-state decode step — TEST INFRASTRUCTURE.
+ * Plain scalar C; see lsq_oracle.h for the sources and the state layout.
+ *
+ * Build: gcc -std=c11 -O2 -fno-fast-math -ffp-contract=off -fPIC -shared -lm -pthread
+ * (no contraction: every fused multiply-add below is an explicit fmaf, every
+ * other fp32 operation rounds once, as written).
+ *
+ * Readings taken where the pages are silent (all stated in the design notes):
+ *  - symmetric codes in [-qmax, qmax], qmax = 2^(bits-1) - 1, no zero point;
+ *  - one fp32 scale per contiguous group of `group` elements along Dk;
+ *  - the decay is folded into the group scale before dequantisation:
+ *      S'[c] = fl(C[c] * fl(s * alpha_c));
+ *  - the output is read from the fp32 state after the update and before it
+ *    is requantised;
+ *  - dynamic scale: fl(absmax/qmax) over the updated group; persistent: the
+ *    frozen scale; yoked: fl(absmax/qmax) over the fp32 reference row after
+ *    the reference's own update at the same step;
+ *  - inv = fl(1/s) (0 for s == 0); codes round the exact product S*inv to
+ *    nearest, ties to even, then clamp to +-qmax;
+ *  - directional rounding: the update of element c is the rank-one write
+ *    w*k_c, with sign sigma_c = sign(w) sign(k_c); the element "moved" from
+ *    its decayed pre-write value S'[c]; both are measured in code units on
+ *    the grid of this step (y = S*inv, y' = S'*inv, exact products).  A
+ *    reversal is a clamped code c1 with (c1 - y') * sigma_c < 0; it is
+ *    replaced by clamp(c1 + sigma_c).
+ */
+#include "lsq_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
+
+int lsqo_check_config(const lsqo_config* cfg) {
+  if (!cfg) return -1;
+  if (cfg->batch < 0 || cfg->heads < 0 || cfg->dk <= 0 || cfg->dv <= 0) return -1;
+  if (cfg->delta != 0 && cfg->delta != 1) return -1;
+  if (cfg->decay != LSQO_DECAY_SCALAR && cfg->decay != LSQO_DECAY_DIAG) return -1;
+  if (cfg->bits == 32) return cfg->policy == LSQO_POLICY_NONE ? 0 : -1;
+  if (cfg->bits != 4 && cfg->bits != 8) return -1;
+  if (cfg->group <= 0 || cfg->dk % cfg->group != 0) return -1;
+  if (cfg->bits == 4 && cfg->dk % 2 != 0) return -1;
+  if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT &&
+      cfg->policy != LSQO_POLICY_YOKED)
+    return -1;
+  if (cfg->rounding != LSQO_ROUND_RNE && cfg->rounding != LSQO_ROUND_BDR) return -1;
+  return 0;
+}
+
+/* round half to even of an exactly represented double */
+static double round_half_even(double y) {
+  double r = floor(y);
+  double frac = y - r; /* exact: y has at most 48 significant bits here */
+  if (frac > 0.5) return r + 1.0;
+  if (frac < 0.5) return r;
+  return (fmod(r, 2.0) == 0.0) ? r : r + 1.0;
+}
+
+static double clampd(double x, double lo, double hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+static int sign_f(float x) { return (x > 0.0f) - (x < 0.0f); }
+
+/* Eq. (1) for one row of an fp32 state (the unquantised mode, and the yoked
+ * reference).  row is updated in place; returns o_r = S_t,r . q. */
+static float fp32_row_update(const lsqo_config* cfg, float* row, const float* q, const float* k,
+                             float v_r, const float* alpha, float beta, float* scratch) {
+  const int dk = cfg->dk;
+  /* S' = S_{t-1} Lambda_t: scalar decay scales the whole row, diagonal decay
+   * scales column c by alpha_c */
+  for (int c = 0; c < dk; ++c) {
+    float a = (cfg->decay == LSQO_DECAY_DIAG) ? alpha[c] : alpha[0];
+    scratch[c] = row[c] * a;
+  }
+  /* delta correction: u = S' k (the part of the state aligned with k) */
+  float u = 0.0f;
+  if (cfg->delta) {
+    double acc = 0.0;
+    for (int c = 0; c < dk; ++c) acc += (double)scratch[c] * (double)k[c];
+    u = (float)acc;
+  }
+  /* S_t = S' (I - delta beta k k^T) + beta v k^T = S' + w k^T, w = beta (v - delta u) */
+  float w = beta * (v_r - u);
+  double o = 0.0;
+  for (int c = 0; c < dk; ++c) {
+    row[c] = fmaf(w, k[c], scratch[c]);
+    o += (double)row[c] * (double)q[c];
+  }
+  return (float)o;
+}
+
+typedef struct {
+  const lsqo_config* cfg;
+  int64_t h0, h1;
+  int8_t* codes;
+  float* scales;
+  float* ref;
+  float* f32;
+  const float *q, *k, *v, *alpha, *beta;
+  float *o, *o_ref;
+  lsqo_stats stats;
+} step_job;
+
+static void step_heads(step_job* J) {
+  const lsqo_config* cfg = J->cfg;
+  const int dk = cfg->dk, dv = cfg->dv;
+  const int diag = cfg->decay == LSQO_DECAY_DIAG;
+  float* sp = (float*)malloc(sizeof(float) * (size_t)dk);   /* S' */
+  float* st = (float*)malloc(sizeof(float) * (size_t)dk);   /* S_t */
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)dk);  /* fp32 scratch */
+  for (int64_t h = J->h0; h < J->h1; ++h) {
+    const float* q = J->q + h * dk;
+    const float* k = J->k + h * dk;
+    const float* v = J->v + h * dv;
+    const float* alpha = J->alpha + (diag ? h * dk : h);
+    const float beta = J->beta[h];
+
+    if (cfg->bits == 32) {
+      for (int r = 0; r < dv; ++r) {
+        float* row = J->f32 + (h * dv + r) * (int64_t)dk;
+        J->o[h * dv + r] = fp32_row_update(cfg, row, q, k, v[r], alpha, beta, tmp);
+      }
+      continue;
+    }
+
+    const int g = cfg->group, ng = dk / g;
+    const int qm = qmax_of(cfg->bits);
+    for (int r = 0; r < dv; ++r) {
+      int8_t* C = J->codes + (h * dv + r) * (int64_t)dk;
+      float* s = J->scales + (h * dv + r) * (int64_t)ng;
+
+      /* yoked arm: advance the fp32 reference row first (same inputs) */
+      float* R = NULL;
+      if (cfg->policy == LSQO_POLICY_YOKED) {
+        R = J->ref + (h * dv + r) * (int64_t)dk;
+        float oref = fp32_row_update(cfg, R, q, k, v[r], alpha, beta, tmp);
+        if (J->o_ref) J->o_ref[h * dv + r] = oref;
+      }
+
+      /* dequantise with the decay folded into the group scale */
+      for (int c = 0; c < dk; ++c) {
+        float a = diag ? alpha[c] : alpha[0];
+        float m = s[c / g] * a;
+        sp[c] = (float)C[c] * m;
+      }
+      float u = 0.0f;
+      if (cfg->delta) {
+        double acc = 0.0;
+        for (int c = 0; c < dk; ++c) acc += (double)sp[c] * (double)k[c];
+        u = (float)acc;
+      }
+      float w = beta * (v[r] - u);
+      double o = 0.0;
+      for (int c = 0; c < dk; ++c) {
+        st[c] = fmaf(w, k[c], sp[c]);
+        o += (double)st[c] * (double)q[c];
+      }
+      J->o[h * dv + r] = (float)o;
+
+      /* scale policy, then requantise group by group */
+      for (int gi = 0; gi < ng; ++gi) {
+        float snew;
+        if (cfg->policy == LSQO_POLICY_PERSISTENT) {
+          snew = s[gi];
+        } else {
+          const float* src = (cfg->policy == LSQO_POLICY_YOKED) ? R : st;
+          float amax = 0.0f;
+          for (int c = gi * g; c < (gi + 1) * g; ++c) {
+            float a = fabsf(src[c]);
+            if (a > amax) amax = a;
+          }
+          snew = amax / (float)qm;
+        }
+        float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
+        for (int c = gi * g; c < (gi + 1) * g; ++c) {
+          double y = (double)st[c] * (double)inv; /* exact */
+          double c0 = round_half_even(y);
+          double c1 = clampd(c0, -qm, qm);
+          if (c1 != c0) J->stats.clamped++;
+          double c2 = c1;
+          if (cfg->rounding == LSQO_ROUND_BDR) {
+            int sigma = sign_f(w) * sign_f(k[c]);
+            double yp = (double)sp[c] * (double)inv; /* exact */
+            int reversed = (sigma > 0 && c1 < yp) || (sigma < 0 && c1 > yp);
+            if (reversed) {
+              c2 = clampd(c1 + sigma, -qm, qm);
+              if (c2 != c1) J->stats.bdr_fired++;
+            }
+          }
+          C[c] = (int8_t)c2;
+        }
+        s[gi] = snew;
+      }
+    }
+  }
+  free(sp);
+  free(st);
+  free(tmp);
+}
+
+int lsqo_step(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref, float* f32,
+              const float* q, const float* k, const float* v, const float* alpha,
+              const float* beta, float* o, float* o_ref, lsqo_stats* stats) {
+  if (lsqo_check_config(cfg)) return -1;
+  step_job J;
+  memset(&J, 0, sizeof J);
+  J.cfg = cfg;
+  J.h0 = 0;
+  J.h1 = (int64_t)cfg->batch * cfg->heads;
+  J.codes = codes; J.scales = scales; J.ref = ref; J.f32 = f32;
+  J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.o = o; J.o_ref = o_ref;
+  step_heads(&J);
+  if (stats) {
+    stats->clamped += J.stats.clamped;
+    stats->bdr_fired += J.stats.bdr_fired;
+  }
+  return 0;
+}
+
+typedef struct {
+  step_job job;
+  int32_t H;
+  int64_t n;
+} run_job;
+
+static void* run_worker(void* arg) {
+  run_job* R = (run_job*)arg;
+  step_job J = R->job;
+  const lsqo_config* cfg = J.cfg;
+  const int64_t n = R->n;
+  const int64_t dk = cfg->dk, dv = cfg->dv;
+  const int64_t astride = (cfg->decay == LSQO_DECAY_DIAG) ? n * dk : n;
+  for (int32_t t = 0; t < R->H; ++t) {
+    J.q = R->job.q + t * n * dk;
+    J.k = R->job.k + t * n * dk;
+    J.v = R->job.v + t * n * dv;
+    J.alpha = R->job.alpha + t * astride;
+    J.beta = R->job.beta + t * n;
+    J.o = R->job.o + t * n * dv;
+    J.o_ref = R->job.o_ref ? R->job.o_ref + t * n * dv : NULL;
+    step_heads(&J);
+  }
+  R->job.stats = J.stats;
+  return NULL;
+}
+
+int lsqo_run(const lsqo_config* cfg, int32_t H, int8_t* codes, float* scales, float* ref,
+             float* f32, const float* q, const float* k, const float* v, const float* alpha,
+             const float* beta, float* o, float* o_ref, int32_t nthreads) {
+  if (lsqo_check_config(cfg) || H < 0) return -1;
+  const int64_t n = (int64_t)cfg->batch * cfg->heads;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n && n > 0) nthreads = (int32_t)n;
+  run_job* jobs = (run_job*)calloc((size_t)nthreads, sizeof(run_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int32_t i = 0; i < nthreads; ++i) {
+    step_job* J = &jobs[i].job;
+    J->cfg = cfg;
+    J->h0 = n * i / nthreads;
+    J->h1 = n * (i + 1) / nthreads;
+    J->codes = codes; J->scales = scales; J->ref = ref; J->f32 = f32;
+    J->q = q; J->k = k; J->v = v; J->alpha = alpha; J->beta = beta; J->o = o; J->o_ref = o_ref;
+    jobs[i].H = H;
+    jobs[i].n = n;
+  }
+  if (nthreads == 1) {
+    run_worker(&jobs[0]);
+  } else {
+    for (int32_t i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, run_worker, &jobs[i]);
+    for (int32_t i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  }
+  free(jobs);
+  free(th);
+  return 0;
+}
+
+int lsqo_calibrate(const lsqo_config* cfg, const float* S, int8_t* codes, float* scales,
+                   float* ref, float* f32) {
+  if (lsqo_check_config(cfg)) return -1;
+  const int64_t n = (int64_t)cfg->batch * cfg->heads;
+  const int64_t rows = n * cfg->dv;
+  const int dk = cfg->dk;
+  if (cfg->bits == 32) {
+    memcpy(f32, S, sizeof(float) * (size_t)(rows * dk));
+    return 0;
+  }
+  const int g = cfg->group, ng = dk / g, qm = qmax_of(cfg->bits);
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* x = S + r * dk;
+    for (int gi = 0; gi < ng; ++gi) {
+      float amax = 0.0f;
+      for (int c = gi * g; c < (gi + 1) * g; ++c) {
+        float a = fabsf(x[c]);
+        if (a > amax) amax = a;
+      }
+      float s = amax / (float)qm;
+      float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+      for (int c = gi * g; c < (gi + 1) * g; ++c) {
+        double y = (double)x[c] * (double)inv;
+        codes[r * dk + c] = (int8_t)clampd(round_half_even(y), -qm, qm);
+      }
+      scales[r * ng + gi] = s;
+    }
+  }
+  if (cfg->policy == LSQO_POLICY_YOKED) memcpy(ref, S, sizeof(float) * (size_t)(rows * dk));
+  return 0;
+}
+
+int lsqo_dequantize(const lsqo_config* cfg, const int8_t* codes, const float* scales, float* out) {
+  if (lsqo_check_config(cfg) || cfg->bits == 32) return -1;
+  const int64_t rows = (int64_t)cfg->batch * cfg->heads * cfg->dv;
+  const int dk = cfg->dk, g = cfg->group, ng = dk / g;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < dk; ++c) out[r * dk + c] = (float)codes[r * dk + c] * scales[r * ng + c / g];
+  return 0;
+}
+
+int lsqo_pack(int32_t bits, int32_t dk, int64_t rows, const int8_t* codes, uint8_t* packed) {
+  if (bits == 8) {
+    for (int64_t i = 0; i < rows * dk; ++i) packed[i] = (uint8_t)codes[i];
+    return 0;
+  }
+  if (bits != 4 || dk % 2) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < dk; c += 2) {
+      uint8_t lo = (uint8_t)codes[r * dk + c] & 0x0F;
+      uint8_t hi = (uint8_t)codes[r * dk + c + 1] & 0x0F;
+      packed[r * (dk / 2) + c / 2] = (uint8_t)(lo | (hi << 4));
+    }
+  return 0;
+}
+
+static int8_t sext4(unsigned nib) { return (int8_t)((nib & 0x8) ? (int)nib - 16 : (int)nib); }
+
+int lsqo_unpack(int32_t bits, int32_t dk, int64_t rows, const uint8_t* packed, int8_t* codes) {
+  if (bits == 8) {
+    for (int64_t i = 0; i < rows * dk; ++i) codes[i] = (int8_t)packed[i];
+    return 0;
+  }
+  if (bits != 4 || dk % 2) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < dk; c += 2) {
+      uint8_t b = packed[r * (dk / 2) + c / 2];
+      codes[r * dk + c] = sext4(b & 0x0F);
+      codes[r * dk + c + 1] = sext4(b >> 4);
+    }
+  return 0;
+}

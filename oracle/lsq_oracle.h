@@ -1,0 +1,103 @@
+/*
+ * CPU oracle for the low-bit recurrent-state decode step — TEST INFRASTRUCTURE.
+ *
+ * Only tests/, the smoke check and the benchmark's CPU-baseline leg may load
+ * this library.  The product path (the HIP library) never links, includes or
+ * calls anything here, and this file includes nothing from the product path.
+ *
+ * The oracle is plain, slow and obviously correct: scalar loops, IEEE fp32
+ * arithmetic where the method computes in fp32 (so that quantisation
+ * decisions are taken in the same precision as on the GPU), double-precision
+ * accumulation for the two dot products, correctly rounded fmaf from libm,
+ * exact products in double for every rounding decision.
+ *
+ * Sources (page title, then the passage):
+ *  - "LinQuant: Functional Invariances for Low-Precision Linear Recurrences"
+ *    (picx.dev summary), Theoretical Foundation, Eq. (1): the general state
+ *    update S_t = S_{t-1} Lambda_t (I - delta beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *    and its structural choices (scalar vs diagonal decay, write gate, delta
+ *    correction).
+ *  - "When Dynamic Scaling Fails: A Scale-State Feedback Governs
+ *    Recurrent-State Quantization..." (abstract and project page): the state
+ *    is requantised at every decode step with uniform group-wise INT4; the
+ *    per-token dynamic scale is read from the state being quantised; the
+ *    persistent (static) scale; the scale yoked to a full-precision reference
+ *    run alongside ("same grid, same bit-width, loop cut").
+ *  - "Preserving Updates in Low-Bit Recurrent State Quantization" (abstract):
+ *    Bounded Directional Rounding rounds an element whose rounded value moved
+ *    opposite to its update one step toward that update.
+ *
+ * State layout used by the oracle (unpacked, host memory, heads = batch*heads):
+ *   codes  int8  [heads][Dv][Dk]        signed codes in [-qmax, qmax]
+ *   scales float [heads][Dv][Dk/group]  one fp32 scale per group along Dk
+ *   ref    float [heads][Dv][Dk]        fp32 reference state (yoked policy)
+ *   f32    float [heads][Dv][Dk]        fp32 state (bits == 32)
+ * Inputs: q,k [heads][Dk]; v [heads][Dv]; alpha [heads] (scalar decay) or
+ * [heads][Dk] (diagonal decay); beta [heads]; outputs o, o_ref [heads][Dv].
+ */
+#ifndef LSQ_ORACLE_H
+#define LSQ_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* enumerations (numeric values mirror the public interface by necessity) */
+enum { LSQO_POLICY_NONE = 0, LSQO_POLICY_DYNAMIC = 1, LSQO_POLICY_PERSISTENT = 2, LSQO_POLICY_YOKED = 3 };
+enum { LSQO_ROUND_RNE = 0, LSQO_ROUND_BDR = 1 };
+enum { LSQO_DECAY_SCALAR = 0, LSQO_DECAY_DIAG = 1 };
+
+typedef struct {
+  int32_t batch, heads, dk, dv;
+  int32_t bits;     /* 4, 8, or 32 (unquantised fp32 state) */
+  int32_t group;    /* group size along Dk (ignored for bits == 32) */
+  int32_t policy;   /* LSQO_POLICY_* */
+  int32_t rounding; /* LSQO_ROUND_* */
+  int32_t delta;    /* 0: linear write, 1: delta-rule correction */
+  int32_t decay;    /* LSQO_DECAY_* */
+} lsqo_config;
+
+/* counters filled by a step (nullable): element-steps whose code was clamped
+ * at +-qmax, and element-steps changed by directional rounding */
+typedef struct {
+  int64_t clamped;
+  int64_t bdr_fired;
+} lsqo_stats;
+
+/* 0 on success, -1 on an invalid configuration */
+int lsqo_check_config(const lsqo_config* cfg);
+
+/* One decode step for every head, in place.  o_ref (nullable) receives the
+ * yoked reference readout R_t q_t. */
+int lsqo_step(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref, float* f32,
+              const float* q, const float* k, const float* v, const float* alpha,
+              const float* beta, float* o, float* o_ref, lsqo_stats* stats);
+
+/* H consecutive steps; inputs carry a leading [H] dimension, o is [H][heads][Dv].
+ * Heads are independent, so they are split over nthreads POSIX threads. */
+int lsqo_run(const lsqo_config* cfg, int32_t H, int8_t* codes, float* scales, float* ref,
+             float* f32, const float* q, const float* k, const float* v, const float* alpha,
+             const float* beta, float* o, float* o_ref, int32_t nthreads);
+
+/* Quantise an fp32 state S [heads][Dv][Dk] into this configuration: one scale
+ * per group from the group's absolute maximum, codes by round-to-nearest-even
+ * and clamp.  The yoked policy also copies S into ref; bits == 32 copies S
+ * into f32. */
+int lsqo_calibrate(const lsqo_config* cfg, const float* S, int8_t* codes, float* scales,
+                   float* ref, float* f32);
+
+/* Dequantised value codes*scale, [heads][Dv][Dk] */
+int lsqo_dequantize(const lsqo_config* cfg, const int8_t* codes, const float* scales, float* out);
+
+/* Packed storage of the codes: row-major [rows][Dk*bits/8] bytes.  INT8: one
+ * two's-complement byte per element.  INT4: element c of a row sits in byte
+ * c/2, low nibble for even c, as a two's-complement nibble. */
+int lsqo_pack(int32_t bits, int32_t dk, int64_t rows, const int8_t* codes, uint8_t* packed);
+int lsqo_unpack(int32_t bits, int32_t dk, int64_t rows, const uint8_t* packed, int8_t* codes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
