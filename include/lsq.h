@@ -1,0 +1,176 @@
+/*
+ * lsq — decode step of a linear recurrence whose matrix state is stored at low
+ * bit-width, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (one decode step, for every batch*head independently):
+ *
+ *   S_t = S_{t-1} Lambda_t (I - delta beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *
+ * is Eq. (1) of "LinQuant: Functional Invariances for Low-Precision Linear
+ * Recurrences" (summary page, Theoretical Foundation), with scalar decay
+ * Lambda_t = alpha_t I or diagonal decay diag(alpha_t), write gate beta_t > 0
+ * and delta in {0,1} (Key structural choices).  S_t is Dv x Dk.  The step
+ * emits o_t = S_t q_t, then requantises the state, as "When Dynamic Scaling
+ * Fails" (abstract) describes: the state is rewritten and requantised at every
+ * decode step with uniform group-wise INT4/INT8, the group scale being
+ *   DYNAMIC    read from the new state itself (per-token absmax; project page,
+ *              mechanism paragraph),
+ *   PERSISTENT frozen once by calibration ("plain persistent scaling"),
+ *   YOKED      read from an fp32 reference state advanced alongside ("the same
+ *              grid, the same bit-width, but the loop cut"),
+ * and rounded either to nearest-even or by Bounded Directional Rounding
+ * ("Preserving Updates in Low-Bit Recurrent State Quantization", abstract): an
+ * element whose rounded value moved opposite to its update is rounded one
+ * grid step toward the update.
+ *
+ * Arithmetic contract (every step below is what the kernels compute):
+ *   m_c   = fl(s_group(c) * alpha_c)            alpha_c = alpha for scalar decay
+ *   S'_c  = fl(C_c * m_c)                       dequantise with the decay folded in
+ *   u     = S' . k (fp32, any summation order)  only when delta = 1, else 0
+ *   w     = fl(beta * fl(v_r - u))
+ *   S_c   = fma(w, k_c, S'_c)
+ *   o_r   = S . q (fp32, any summation order)   read before requantisation
+ *   s_new = DYNAMIC: fl(max|S_c| / qmax) per group; PERSISTENT: s;
+ *           YOKED: fl(max|R_c| / qmax) with R advanced by the same update in fp32
+ *   inv   = s_new == 0 ? 0 : fl(1 / s_new)
+ *   c1    = clamp(round-half-even(S_c * inv exactly), -qmax, qmax)
+ *   BDR:    sigma_c = sign(w) sign(k_c); if (c1 - S'_c * inv) * sigma_c < 0
+ *           (exact), then c = clamp(c1 + sigma_c), else c = c1
+ * with qmax = 2^(bits-1) - 1 (7 for INT4, 127 for INT8).
+ *
+ * Memory: every pointer below is a DEVICE pointer (row-major, 16-byte
+ * aligned) unless stated.  The library never allocates device memory: the
+ * caller allocates the state buffers (lsq_state_sizes gives their sizes) and
+ * the inputs/outputs, and binds them to a handle.  The handle itself is a
+ * small host object.
+ *
+ * Packed state layout (per handle, heads = batch*heads):
+ *   codes  [heads][Dv][Dk*bits/8] bytes.  INT8: one two's-complement byte per
+ *          element.  INT4: element c of a row in byte c/2, low nibble for even
+ *          c, two's-complement nibble.  Codes lie in [-qmax, qmax].
+ *   scales [heads][Dv][Dk/group] fp32, one per contiguous group along Dk.
+ *   ref    [heads][Dv][Dk] fp32, the yoked policy's reference state.
+ *   f32    [heads][Dv][Dk] fp32, the state of the unquantised mode (bits 32).
+ * Inputs per step: q, k [heads][Dk]; v [heads][Dv]; alpha [heads] (scalar
+ * decay) or [heads][Dk] (diagonal); beta [heads].  Output o [heads][Dv];
+ * o_ref [heads][Dv] (yoked only, nullable).
+ *
+ * Errors and streams: calls are asynchronous on the given HIP stream (a
+ * hipStream_t passed as void*, NULL for the default stream).  Argument checks
+ * happen on the host before any launch and return a status without touching
+ * the device.  Launch failures return LSQ_ERR_HIP.  No C++ exception crosses
+ * the ABI.  A handle must not be used on two streams at once.  Inputs must be
+ * finite; the data is not scanned.  With batch*heads == 0 every call is a
+ * no-op and its data pointers may be NULL.
+ */
+#ifndef LSQ_H
+#define LSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSQ_OK = 0,
+  LSQ_ERR_INVALID_ARG = 1,     /* null pointer, bad value, misaligned buffer */
+  LSQ_ERR_UNSUPPORTED = 2,     /* a valid configuration this build has no kernel for */
+  LSQ_ERR_BUFFER_TOO_SMALL = 3,
+  LSQ_ERR_NOT_CALIBRATED = 4,  /* persistent policy stepped before its scales were frozen */
+  LSQ_ERR_HIP = 5              /* a HIP runtime call or kernel launch failed */
+} lsq_status;
+
+typedef enum {
+  LSQ_POLICY_NONE = 0,        /* bits == 32: unquantised fp32 state */
+  LSQ_POLICY_DYNAMIC = 1,
+  LSQ_POLICY_PERSISTENT = 2,
+  LSQ_POLICY_YOKED = 3
+} lsq_policy;
+
+typedef enum { LSQ_ROUND_RNE = 0, LSQ_ROUND_BDR = 1 } lsq_rounding;
+typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
+
+/* Shape, format and method flags of one handle.
+ *   bits   4, 8 (quantised) or 32 (fp32 state, policy NONE)
+ *   group  group size along Dk; must divide dk.  This build supports
+ *          INT4 groups of 32/64/128 and INT8 groups of 16/32/64/128 (a group
+ *          never smaller than the 16 bytes one lane owns), Dk in {64, 128}.
+ *   delta  0: linear write, 1: delta-rule correction
+ */
+typedef struct {
+  int32_t batch, heads, dk, dv;
+  int32_t bits, group, policy, rounding, delta, decay;
+} lsq_config;
+
+/* Caller-owned device buffers and their capacities in bytes.  Buffers the
+ * configuration does not use may be NULL with capacity 0. */
+typedef struct {
+  void* codes;   size_t codes_bytes;
+  float* scales; size_t scales_bytes;
+  float* ref;    size_t ref_bytes;
+  float* f32;    size_t f32_bytes;
+} lsq_buffers;
+
+typedef struct lsq_state lsq_state;
+
+/* Byte sizes of the state buffers a configuration needs (0 when unused).
+ * Host only.  Any output pointer may be NULL. */
+lsq_status lsq_state_sizes(const lsq_config* cfg, size_t* codes_bytes, size_t* scales_bytes,
+                           size_t* ref_bytes, size_t* f32_bytes);
+
+/* Create a handle that binds the caller's buffers.  Allocates only the host
+ * handle.  Checks: valid config, non-null and 16-byte aligned buffers for
+ * what the config uses, capacities >= lsq_state_sizes.  The buffer contents
+ * are not read.  A persistent-policy handle starts uncalibrated. */
+lsq_status lsq_state_alloc(const lsq_config* cfg, const lsq_buffers* bufs, lsq_state** out);
+
+/* Destroy a handle (the device buffers stay the caller's).  NULL is a no-op. */
+void lsq_state_free(lsq_state* st);
+
+/* Copy of the handle's configuration (host). */
+lsq_status lsq_state_config(const lsq_state* st, lsq_config* out);
+
+/* S_0 = 0: zero codes, scales, ref and f32 with a fill kernel (capturable in
+ * a HIP graph).  A persistent-policy handle becomes uncalibrated. */
+lsq_status lsq_state_zero(lsq_state* st, void* stream);
+
+/* Load an fp32 state S [heads][Dv][Dk] (device) into the handle: one scale per
+ * group s = fl(absmax/qmax), codes clamp(RNE(S * fl(1/s))); the yoked policy
+ * also copies S into ref; bits 32 copies S into f32.  Freezes the scales of a
+ * persistent-policy handle (marks it calibrated).  This is the calibration of
+ * "plain persistent scaling" ("When Dynamic Scaling Fails", abstract). */
+lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream);
+
+/* Declare that the bound scale buffer already holds frozen scales (resuming a
+ * persistent-policy state from a copy of its buffers). */
+lsq_status lsq_state_set_calibrated(lsq_state* st, int32_t calibrated);
+
+/* One decode step for all heads (shapes above).  alpha has [heads] or
+ * [heads][Dk] entries by the decay flag.  o_ref may be NULL; it is written
+ * only by the yoked policy.  The state is updated in place. */
+lsq_status lsq_decode_step(lsq_state* st, const float* q, const float* k, const float* v,
+                           const float* alpha, const float* beta, float* o, float* o_ref,
+                           void* stream);
+
+/* H sequential decode steps ("decode horizon H"); every input carries a
+ * leading [H] axis (contiguous, step-major), o (and o_ref) receive
+ * [H][heads][Dv].  The state round-trips through device memory every step. */
+lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float* k,
+                          const float* v, const float* alpha, const float* beta, float* o,
+                          float* o_ref, void* stream);
+
+/* Static description of a status code. */
+const char* lsq_status_string(lsq_status s);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* lsq_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t lsq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSQ_H */

@@ -72,13 +72,15 @@ def lib():
             cfgp = ctypes.POINTER(_Config)
             L.lsqo_check_config.argtypes = [cfgp]
             L.lsqo_step.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(_Stats)]
+            L.lsqo_step_trace.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P, P,
+                                          ctypes.POINTER(_Stats), P, P]
             L.lsqo_run.argtypes = [cfgp, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_int32]
             L.lsqo_calibrate.argtypes = [cfgp, P, P, P, P, P]
             L.lsqo_dequantize.argtypes = [cfgp, P, P, P]
             L.lsqo_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
             L.lsqo_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
-            for f in (L.lsqo_check_config, L.lsqo_step, L.lsqo_run, L.lsqo_calibrate,
+            for f in (L.lsqo_check_config, L.lsqo_step, L.lsqo_step_trace, L.lsqo_run, L.lsqo_calibrate,
                       L.lsqo_dequantize, L.lsqo_pack, L.lsqo_unpack):
                 f.restype = ctypes.c_int
             _lib = L
@@ -170,19 +172,27 @@ def _inputs(cfg, q, k, v, alpha, beta, lead=()):
     return q, k, v, alpha, beta
 
 
-def step(cfg: OracleConfig, st: OracleState, q, k, v, alpha, beta, stats: dict | None = None):
+def step(cfg: OracleConfig, st: OracleState, q, k, v, alpha, beta, stats: dict | None = None,
+         trace: dict | None = None):
     """One decode step of every head, in place on ``st``.
 
-    Returns (o, o_ref); o_ref is None unless the policy is yoked.
+    Returns (o, o_ref); o_ref is None unless the policy is yoked.  With a
+    ``trace`` dict (quantised states only), trace["y"] and trace["yp"] receive
+    the exact pre-rounding values S_t*inv and S'*inv in code units.
     """
     _check(cfg)
     q, k, v, alpha, beta = _inputs(cfg, q, k, v, alpha, beta)
     o = np.empty((cfg.n, cfg.dv), np.float32)
     o_ref = np.empty((cfg.n, cfg.dv), np.float32) if cfg.policy == POLICY_YOKED else None
     s = _Stats()
-    rc = lib().lsqo_step(ctypes.byref(cfg.c()), _p(st.codes), _p(st.scales), _p(st.ref),
-                         _p(st.f32), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o), _p(o_ref),
-                         ctypes.byref(s))
+    y = yp = None
+    if trace is not None and cfg.bits != 32:
+        y = np.zeros((cfg.n, cfg.dv, cfg.dk), np.float64)
+        yp = np.zeros((cfg.n, cfg.dv, cfg.dk), np.float64)
+        trace["y"], trace["yp"] = y, yp
+    rc = lib().lsqo_step_trace(ctypes.byref(cfg.c()), _p(st.codes), _p(st.scales), _p(st.ref),
+                               _p(st.f32), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o),
+                               _p(o_ref), ctypes.byref(s), _p(y), _p(yp))
     if rc:
         raise RuntimeError("oracle step failed")
     if stats is not None:

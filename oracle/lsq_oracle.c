@@ -100,6 +100,7 @@ typedef struct {
   float* f32;
   const float *q, *k, *v, *alpha, *beta;
   float *o, *o_ref;
+  double *y_out, *yp_out; /* nullable: exact code-unit values before rounding */
   lsqo_stats stats;
 } step_job;
 
@@ -176,6 +177,10 @@ static void step_heads(step_job* J) {
         float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
         for (int c = gi * g; c < (gi + 1) * g; ++c) {
           double y = (double)st[c] * (double)inv; /* exact */
+          if (J->y_out) {
+            J->y_out[(h * dv + r) * (int64_t)dk + c] = y;
+            J->yp_out[(h * dv + r) * (int64_t)dk + c] = (double)sp[c] * (double)inv;
+          }
           double c0 = round_half_even(y);
           double c1 = clampd(c0, -qm, qm);
           if (c1 != c0) J->stats.clamped++;
@@ -203,7 +208,16 @@ static void step_heads(step_job* J) {
 int lsqo_step(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref, float* f32,
               const float* q, const float* k, const float* v, const float* alpha,
               const float* beta, float* o, float* o_ref, lsqo_stats* stats) {
+  return lsqo_step_trace(cfg, codes, scales, ref, f32, q, k, v, alpha, beta, o, o_ref, stats,
+                         NULL, NULL);
+}
+
+int lsqo_step_trace(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref,
+                    float* f32, const float* q, const float* k, const float* v,
+                    const float* alpha, const float* beta, float* o, float* o_ref,
+                    lsqo_stats* stats, double* y_out, double* yp_out) {
   if (lsqo_check_config(cfg)) return -1;
+  if ((y_out == NULL) != (yp_out == NULL)) return -1;
   step_job J;
   memset(&J, 0, sizeof J);
   J.cfg = cfg;
@@ -211,6 +225,7 @@ int lsqo_step(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref, 
   J.h1 = (int64_t)cfg->batch * cfg->heads;
   J.codes = codes; J.scales = scales; J.ref = ref; J.f32 = f32;
   J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.o = o; J.o_ref = o_ref;
+  J.y_out = y_out; J.yp_out = yp_out;
   step_heads(&J);
   if (stats) {
     stats->clamped += J.stats.clamped;

@@ -75,6 +75,15 @@ int lsqo_step(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref, 
               const float* q, const float* k, const float* v, const float* alpha,
               const float* beta, float* o, float* o_ref, lsqo_stats* stats);
 
+/* lsqo_step that also records, for every quantised element, the exact
+ * pre-rounding values in code units: y = S_t * inv and y' = S' * inv (both
+ * nullable together).  Used to judge whether a differing code lies at a
+ * rounding boundary. */
+int lsqo_step_trace(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref,
+                    float* f32, const float* q, const float* k, const float* v,
+                    const float* alpha, const float* beta, float* o, float* o_ref,
+                    lsqo_stats* stats, double* y_out, double* yp_out);
+
 /* H consecutive steps; inputs carry a leading [H] dimension, o is [H][heads][Dv].
  * Heads are independent, so they are split over nthreads POSIX threads. */
 int lsqo_run(const lsqo_config* cfg, int32_t H, int8_t* codes, float* scales, float* ref,

@@ -1,0 +1,203 @@
+"""Low-bit recurrent-state decode step for MI355X: Python binding of liblsq.so.
+
+The functions below carry the names of the C ABI in ``include/lsq.h`` and do
+argument marshalling only; PyTorch provides device memory and streams.  Every
+step of the decode path runs in the library's HIP kernels.  Importing this
+package does not load the library; the first call does, and fails loudly if
+it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, asdict
+
+from . import _lib
+from ._lib import LsqError
+
+POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
+ROUND_RNE, ROUND_BDR = 0, 1
+DECAY_SCALAR, DECAY_DIAG = 0, 1
+
+__all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_alloc",
+           "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_set_calibrated",
+           "lsq_decode_step", "lsq_decode_run", "lsq_status_string", "lsq_version"]
+
+
+@dataclass(frozen=True)
+class LsqConfig:
+    """Mirror of ``lsq_config``."""
+    batch: int
+    heads: int
+    dk: int
+    dv: int
+    bits: int = 4
+    group: int = 32
+    policy: int = POLICY_PERSISTENT
+    rounding: int = ROUND_RNE
+    delta: int = 0
+    decay: int = DECAY_SCALAR
+
+    @property
+    def n(self) -> int:
+        return self.batch * self.heads
+
+    def c(self) -> _lib.lsq_config:
+        return _lib.lsq_config(**asdict(self))
+
+
+def _stream_ptr(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def lsq_state_sizes(cfg: LsqConfig) -> tuple[int, int, int, int]:
+    """(codes, scales, ref, f32) byte sizes of the state buffers."""
+    L = _lib.load()
+    out = [ctypes.c_size_t(0) for _ in range(4)]
+    _lib.check(L.lsq_state_sizes(ctypes.byref(cfg.c()), *map(ctypes.byref, out)),
+               "lsq_state_sizes")
+    return tuple(int(x.value) for x in out)
+
+
+def lsq_state_alloc(cfg: LsqConfig, codes=None, scales=None, ref=None, f32=None) -> int:
+    """Bind caller-owned device tensors to a new handle (returns the handle)."""
+    L = _lib.load()
+    nb = lambda t: 0 if t is None else t.numel() * t.element_size()
+    bufs = _lib.lsq_buffers(_ptr(codes), nb(codes), _ptr(scales), nb(scales), _ptr(ref), nb(ref),
+                            _ptr(f32), nb(f32))
+    h = ctypes.c_void_p()
+    _lib.check(L.lsq_state_alloc(ctypes.byref(cfg.c()), ctypes.byref(bufs), ctypes.byref(h)),
+               "lsq_state_alloc")
+    return h.value
+
+
+def lsq_state_free(handle: int) -> None:
+    _lib.load().lsq_state_free(handle)
+
+
+def lsq_state_zero(handle: int, stream=None) -> None:
+    _lib.check(_lib.load().lsq_state_zero(handle, _stream_ptr(stream)), "lsq_state_zero")
+
+
+def lsq_state_calibrate(handle: int, S, stream=None) -> None:
+    _lib.check(_lib.load().lsq_state_calibrate(handle, _ptr(S), _stream_ptr(stream)),
+               "lsq_state_calibrate")
+
+
+def lsq_state_set_calibrated(handle: int, calibrated: bool = True) -> None:
+    _lib.check(_lib.load().lsq_state_set_calibrated(handle, int(bool(calibrated))),
+               "lsq_state_set_calibrated")
+
+
+def lsq_decode_step(handle: int, q, k, v, alpha, beta, o, o_ref=None, stream=None) -> None:
+    _lib.check(_lib.load().lsq_decode_step(handle, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                           _ptr(beta), _ptr(o), _ptr(o_ref), _stream_ptr(stream)),
+               "lsq_decode_step")
+
+
+def lsq_decode_run(handle: int, H: int, q, k, v, alpha, beta, o, o_ref=None, stream=None) -> None:
+    _lib.check(_lib.load().lsq_decode_run(handle, int(H), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                          _ptr(beta), _ptr(o), _ptr(o_ref), _stream_ptr(stream)),
+               "lsq_decode_run")
+
+
+def lsq_status_string(status: int) -> str:
+    return _lib.load().lsq_status_string(int(status)).decode()
+
+
+def lsq_version() -> int:
+    return int(_lib.load().lsq_version())
+
+
+class LsqState:
+    """A handle plus the torch device buffers it binds (codes, scales, ref, f32)."""
+
+    def __init__(self, cfg: LsqConfig, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        _, _, n_ref, n_f32 = lsq_state_sizes(cfg)
+        n, dv, dk = cfg.n, cfg.dv, cfg.dk
+        self.codes = self.scales = self.ref = self.f32 = None
+        if cfg.bits != 32:
+            self.codes = torch.empty((n, dv, dk * cfg.bits // 8), dtype=torch.uint8,
+                                     device=self.device)
+            self.scales = torch.empty((n, dv, dk // cfg.group), dtype=torch.float32,
+                                      device=self.device)
+        if n_ref:
+            self.ref = torch.empty((n, dv, dk), dtype=torch.float32, device=self.device)
+        if cfg.bits == 32:
+            self.f32 = torch.empty((n, dv, dk), dtype=torch.float32, device=self.device)
+        self.handle = lsq_state_alloc(cfg, self.codes, self.scales, self.ref, self.f32)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                lsq_state_free(h)
+            except Exception:
+                pass
+            self.handle = None
+
+    def zero(self, stream=None):
+        lsq_state_zero(self.handle, stream)
+        return self
+
+    def calibrate(self, S, stream=None):
+        _check_tensor("S", S, (self.cfg.n, self.cfg.dv, self.cfg.dk))
+        lsq_state_calibrate(self.handle, S, stream)
+        return self
+
+    def set_calibrated(self, calibrated=True):
+        lsq_state_set_calibrated(self.handle, calibrated)
+        return self
+
+    def _out(self, o, lead):
+        import torch
+        if o is None:
+            o = torch.empty(lead + (self.cfg.n, self.cfg.dv), device=self.device,
+                            dtype=torch.float32)
+        return o
+
+    def _check_inputs(self, q, k, v, alpha, beta, lead=()):
+        c = self.cfg
+        _check_tensor("q", q, lead + (c.n, c.dk))
+        _check_tensor("k", k, lead + (c.n, c.dk))
+        _check_tensor("v", v, lead + (c.n, c.dv))
+        _check_tensor("alpha", alpha, lead + ((c.n, c.dk) if c.decay == DECAY_DIAG else (c.n,)))
+        _check_tensor("beta", beta, lead + (c.n,))
+
+    def step(self, q, k, v, alpha, beta, o=None, o_ref=None, stream=None):
+        """One decode step; returns o (and o_ref for the yoked policy)."""
+        self._check_inputs(q, k, v, alpha, beta)
+        o = self._out(o, ())
+        if self.cfg.policy == POLICY_YOKED and o_ref is None:
+            o_ref = self._out(None, ())
+        lsq_decode_step(self.handle, q, k, v, alpha, beta, o, o_ref, stream)
+        return (o, o_ref) if self.cfg.policy == POLICY_YOKED else o
+
+    def run(self, q, k, v, alpha, beta, o=None, o_ref=None, stream=None):
+        """H decode steps (inputs with a leading [H] axis); returns o [H, n, Dv]."""
+        H = int(q.shape[0])
+        self._check_inputs(q, k, v, alpha, beta, lead=(H,))
+        o = self._out(o, (H,))
+        if self.cfg.policy == POLICY_YOKED and o_ref is None:
+            o_ref = self._out(None, (H,))
+        lsq_decode_run(self.handle, H, q, k, v, alpha, beta, o, o_ref, stream)
+        return (o, o_ref) if self.cfg.policy == POLICY_YOKED else o
+
+
+def _check_tensor(name, t, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")

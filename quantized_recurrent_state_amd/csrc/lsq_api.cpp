@@ -1,0 +1,314 @@
+// Host side of the C ABI in include/lsq.h: validation, handles, launch
+// geometry and dispatch.  All device work is in the .hip translation units.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/lsq.h"
+#include "lsq_internal.h"
+
+struct lsq_state {
+  lsq_config cfg;
+  void* codes;
+  float* scales;
+  float* ref;
+  float* f32;
+  int32_t calibrated;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lsq_status fail(lsq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lsq_status fail(lsq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+lsq_status ok() {
+  g_last_error.clear();
+  return LSQ_OK;
+}
+
+int64_t n_heads(const lsq_config& c) { return (int64_t)c.batch * c.heads; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Checks that make a configuration meaningless (INVALID_ARG) and the ones this
+// build has no kernel for (UNSUPPORTED).
+lsq_status check_config(const lsq_config* c) {
+  if (!c) return fail(LSQ_ERR_INVALID_ARG, "config is null");
+  if (c->batch < 0 || c->heads < 0) return fail(LSQ_ERR_INVALID_ARG, "negative batch or heads");
+  if (c->dk <= 0 || c->dv <= 0) return fail(LSQ_ERR_INVALID_ARG, "dk and dv must be positive");
+  if (c->delta != 0 && c->delta != 1) return fail(LSQ_ERR_INVALID_ARG, "delta must be 0 or 1");
+  if (c->decay != LSQ_DECAY_SCALAR && c->decay != LSQ_DECAY_DIAG)
+    return fail(LSQ_ERR_INVALID_ARG, "decay must be SCALAR or DIAG");
+  if (c->rounding != LSQ_ROUND_RNE && c->rounding != LSQ_ROUND_BDR)
+    return fail(LSQ_ERR_INVALID_ARG, "rounding must be RNE or BDR");
+  if (c->bits == 32) {
+    if (c->policy != LSQ_POLICY_NONE)
+      return fail(LSQ_ERR_INVALID_ARG, "an fp32 state (bits 32) takes policy NONE");
+  } else if (c->bits == 4 || c->bits == 8) {
+    if (c->policy != LSQ_POLICY_DYNAMIC && c->policy != LSQ_POLICY_PERSISTENT &&
+        c->policy != LSQ_POLICY_YOKED)
+      return fail(LSQ_ERR_INVALID_ARG, "a quantised state takes policy DYNAMIC, PERSISTENT or YOKED");
+    if (c->group <= 0 || c->dk % c->group != 0)
+      return fail(LSQ_ERR_INVALID_ARG, "group must be positive and divide dk");
+  } else {
+    return fail(LSQ_ERR_INVALID_ARG, "bits must be 4, 8 or 32");
+  }
+  if (c->dk != 64 && c->dk != 128) return fail(LSQ_ERR_UNSUPPORTED, "dk %d: this build has dk 64 and 128", c->dk);
+  if (c->bits != 32) {
+    const int epl = 128 / c->bits;   // elements one lane owns (16 bytes)
+    if (c->group < epl || (c->group & (c->group - 1)) != 0)
+      return fail(LSQ_ERR_UNSUPPORTED,
+                  "group %d: this build needs a power-of-two group of at least %d elements "
+                  "for %d-bit codes", c->group, epl, c->bits);
+  }
+  const lsq::Geometry g = lsq::geometry(c->bits, c->dk);
+  const int64_t iters = (c->dv + g.rows_per_iter - 1) / g.rows_per_iter;
+  if (n_heads(*c) * iters > INT32_MAX / 2)
+    return fail(LSQ_ERR_UNSUPPORTED, "batch*heads*dv too large for one launch");
+  return ok();
+}
+
+void sizes_of(const lsq_config& c, size_t* codes, size_t* scales, size_t* ref, size_t* f32) {
+  const size_t elems = (size_t)n_heads(c) * c.dv * c.dk;
+  *codes = *scales = *ref = *f32 = 0;
+  if (c.bits == 32) {
+    *f32 = elems * 4;
+    return;
+  }
+  *codes = elems * c.bits / 8;
+  *scales = (size_t)n_heads(c) * c.dv * (c.dk / c.group) * 4;
+  if (c.policy == LSQ_POLICY_YOKED) *ref = elems * 4;
+}
+
+// Launch geometry: one wave per (head, slice of nit row-iterations); slices
+// shrink until there are enough waves to fill the chip.
+void choose_slices(const lsq_config& c, int32_t* nit, int32_t* wph, int32_t* total) {
+  const lsq::Geometry g = lsq::geometry(c.bits, c.dk);
+  const int32_t iters = (c.dv + g.rows_per_iter - 1) / g.rows_per_iter;
+  const int64_t heads = n_heads(c);
+  constexpr int64_t kTargetWaves = 8192;     // 256 CUs x 32 waves
+  int32_t it = iters;
+  while (it > 1 && heads * ((iters + it - 1) / it) < kTargetWaves) it = (it + 1) / 2;
+  *nit = it;
+  *wph = (iters + it - 1) / it;
+  *total = (int32_t)(heads * *wph);
+}
+
+lsq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LSQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+lsq_status check_step_ptrs(const lsq_state* st, const float* q, const float* k, const float* v,
+                           const float* alpha, const float* beta, const float* o) {
+  if (!q || !k || !v || !alpha || !beta || !o)
+    return fail(LSQ_ERR_INVALID_ARG, "q, k, v, alpha, beta and o must be non-null");
+  if (!aligned16(q) || !aligned16(k) || (st->cfg.decay == LSQ_DECAY_DIAG && !aligned16(alpha)))
+    return fail(LSQ_ERR_INVALID_ARG, "q, k (and a diagonal alpha) must be 16-byte aligned");
+  if (!aligned4(v) || !aligned4(alpha) || !aligned4(beta) || !aligned4(o))
+    return fail(LSQ_ERR_INVALID_ARG, "v, alpha, beta and o must be 4-byte aligned");
+  return ok();
+}
+
+lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const float* v,
+                           const float* alpha, const float* beta, float* o, float* o_ref,
+                           hipStream_t stream) {
+  const lsq_config& c = st->cfg;
+  if (n_heads(c) == 0) return ok();
+  lsq::StepArgs a{};
+  a.codes = static_cast<uint8_t*>(st->codes);
+  a.scales = st->scales;
+  a.ref = (c.bits == 32) ? st->f32 : st->ref;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
+  a.o_ref = (c.policy == LSQ_POLICY_YOKED) ? o_ref : nullptr;
+  a.n_heads = (int32_t)n_heads(c);
+  a.dv = c.dv;
+  a.group = c.group;
+  a.ng = (c.bits == 32) ? 0 : c.dk / c.group;
+  choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves);
+  hipError_t e;
+  if (c.bits == 32)
+    e = lsq::launch_step_f32(a, c.dk, c.delta, c.decay, stream);
+  else if (c.bits == 4)
+    e = lsq::launch_step_q4(a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
+  else
+    e = lsq::launch_step_q8(a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
+  return hip_status(e, "decode-step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+lsq_status lsq_state_sizes(const lsq_config* cfg, size_t* codes_bytes, size_t* scales_bytes,
+                           size_t* ref_bytes, size_t* f32_bytes) {
+  lsq_status s = check_config(cfg);
+  if (s != LSQ_OK) return s;
+  size_t a, b, c, d;
+  sizes_of(*cfg, &a, &b, &c, &d);
+  if (codes_bytes) *codes_bytes = a;
+  if (scales_bytes) *scales_bytes = b;
+  if (ref_bytes) *ref_bytes = c;
+  if (f32_bytes) *f32_bytes = d;
+  return ok();
+}
+
+lsq_status lsq_state_alloc(const lsq_config* cfg, const lsq_buffers* bufs, lsq_state** out) {
+  if (!out) return fail(LSQ_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  lsq_status s = check_config(cfg);
+  if (s != LSQ_OK) return s;
+  if (!bufs) return fail(LSQ_ERR_INVALID_ARG, "buffers are null");
+  size_t need[4];
+  sizes_of(*cfg, &need[0], &need[1], &need[2], &need[3]);
+  const void* ptr[4] = {bufs->codes, bufs->scales, bufs->ref, bufs->f32};
+  const size_t cap[4] = {bufs->codes_bytes, bufs->scales_bytes, bufs->ref_bytes, bufs->f32_bytes};
+  static const char* names[4] = {"codes", "scales", "ref", "f32"};
+  for (int i = 0; i < 4; ++i) {
+    if (need[i] == 0) continue;
+    if (!ptr[i]) return fail(LSQ_ERR_INVALID_ARG, "%s buffer is null", names[i]);
+    if (!aligned16(ptr[i])) return fail(LSQ_ERR_INVALID_ARG, "%s buffer is not 16-byte aligned", names[i]);
+    if (cap[i] < need[i])
+      return fail(LSQ_ERR_BUFFER_TOO_SMALL, "%s buffer holds %zu bytes, needs %zu", names[i],
+                  cap[i], need[i]);
+  }
+  lsq_state* st = new (std::nothrow) lsq_state;
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "host allocation of the handle failed");
+  st->cfg = *cfg;
+  st->codes = need[0] ? bufs->codes : nullptr;
+  st->scales = need[1] ? bufs->scales : nullptr;
+  st->ref = need[2] ? bufs->ref : nullptr;
+  st->f32 = need[3] ? bufs->f32 : nullptr;
+  st->calibrated = 0;
+  *out = st;
+  return ok();
+}
+
+void lsq_state_free(lsq_state* st) { delete st; }
+
+lsq_status lsq_state_config(const lsq_state* st, lsq_config* out) {
+  if (!st || !out) return fail(LSQ_ERR_INVALID_ARG, "null argument");
+  *out = st->cfg;
+  return ok();
+}
+
+lsq_status lsq_state_zero(lsq_state* st, void* stream) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  size_t need[4];
+  sizes_of(st->cfg, &need[0], &need[1], &need[2], &need[3]);
+  void* ptr[4] = {st->codes, st->scales, st->ref, st->f32};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < 4; ++i) {
+    if (!need[i]) continue;
+    lsq_status s = hip_status(lsq::launch_fill_zero(ptr[i], need[i], hs), "zero fill");
+    if (s != LSQ_OK) return s;
+  }
+  st->calibrated = 0;
+  return ok();
+}
+
+lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  const lsq_config& c = st->cfg;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t elems = (size_t)n_heads(c) * c.dv * c.dk;
+  if (elems == 0) {   // nothing to read or write
+    st->calibrated = 1;
+    return ok();
+  }
+  if (!S) return fail(LSQ_ERR_INVALID_ARG, "S is null");
+  if (!aligned16(S)) return fail(LSQ_ERR_INVALID_ARG, "S must be 16-byte aligned");
+  if (c.bits == 32) {
+    lsq_status s = hip_status(hipMemcpyAsync(st->f32, S, elems * 4, hipMemcpyDeviceToDevice, hs),
+                              "calibrate copy");
+    if (s == LSQ_OK) st->calibrated = 1;
+    return s;
+  }
+  lsq::CalibArgs a{};
+  a.S = S;
+  a.codes = static_cast<uint8_t*>(st->codes);
+  a.scales = st->scales;
+  a.ref = (c.policy == LSQ_POLICY_YOKED) ? st->ref : nullptr;
+  a.n_heads = (int32_t)n_heads(c);
+  a.dv = c.dv;
+  a.group = c.group;
+  a.ng = c.dk / c.group;
+  choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves);
+  lsq_status s = hip_status(lsq::launch_calibrate(a, c.bits, c.dk, hs), "calibrate launch");
+  if (s == LSQ_OK) st->calibrated = 1;
+  return s;
+}
+
+lsq_status lsq_state_set_calibrated(lsq_state* st, int32_t calibrated) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  st->calibrated = calibrated ? 1 : 0;
+  return ok();
+}
+
+lsq_status lsq_decode_step(lsq_state* st, const float* q, const float* k, const float* v,
+                           const float* alpha, const float* beta, float* o, float* o_ref,
+                           void* stream) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  if (st->cfg.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
+    return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");
+  if (n_heads(st->cfg) == 0) return ok();   // nothing to read or write
+  lsq_status s = check_step_ptrs(st, q, k, v, alpha, beta, o);
+  if (s != LSQ_OK) return s;
+  return launch_one_step(st, q, k, v, alpha, beta, o, o_ref, static_cast<hipStream_t>(stream));
+}
+
+lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float* k,
+                          const float* v, const float* alpha, const float* beta, float* o,
+                          float* o_ref, void* stream) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  if (H < 0) return fail(LSQ_ERR_INVALID_ARG, "negative horizon");
+  if (st->cfg.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
+    return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");
+  if (H == 0 || n_heads(st->cfg) == 0) return ok();   // nothing to read or write
+  lsq_status s = check_step_ptrs(st, q, k, v, alpha, beta, o);
+  if (s != LSQ_OK) return s;
+  const lsq_config& c = st->cfg;
+  const size_t n = (size_t)n_heads(c);
+  const size_t sq = n * c.dk, sv = n * c.dv;
+  const size_t sa = (c.decay == LSQ_DECAY_DIAG) ? n * c.dk : n;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (int32_t t = 0; t < H; ++t) {
+    s = launch_one_step(st, q + t * sq, k + t * sq, v + t * sv, alpha + t * sa, beta + t * n,
+                        o + t * sv, o_ref ? o_ref + t * sv : nullptr, hs);
+    if (s != LSQ_OK) return s;
+  }
+  return ok();
+}
+
+const char* lsq_status_string(lsq_status s) {
+  switch (s) {
+    case LSQ_OK: return "LSQ_OK";
+    case LSQ_ERR_INVALID_ARG: return "LSQ_ERR_INVALID_ARG: invalid argument";
+    case LSQ_ERR_UNSUPPORTED: return "LSQ_ERR_UNSUPPORTED: configuration not supported by this build";
+    case LSQ_ERR_BUFFER_TOO_SMALL: return "LSQ_ERR_BUFFER_TOO_SMALL: a state buffer is too small";
+    case LSQ_ERR_NOT_CALIBRATED: return "LSQ_ERR_NOT_CALIBRATED: persistent scales not calibrated";
+    case LSQ_ERR_HIP: return "LSQ_ERR_HIP: HIP runtime error";
+  }
+  return "unknown lsq_status";
+}
+
+const char* lsq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t lsq_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the host API (lsq_api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/lsq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lsq {
+
+// Arguments of one decode-step launch (one handle, one step).
+struct StepArgs {
+  uint8_t* codes;        // [n][dv][dk*bits/8]
+  float* scales;         // [n][dv][ng]
+  float* ref;            // [n][dv][dk]  yoked reference (or fp32 state for bits 32)
+  const float* q;        // [n][dk]
+  const float* k;        // [n][dk]
+  const float* v;        // [n][dv]
+  const float* alpha;    // [n] or [n][dk]
+  const float* beta;     // [n]
+  float* o;              // [n][dv]
+  float* o_ref;          // [n][dv] or null
+  int32_t n_heads;
+  int32_t dv;
+  int32_t group;
+  int32_t ng;            // groups per row = dk / group
+  int32_t nit;           // row-iterations per wave
+  int32_t waves_per_head;
+  int32_t total_waves;
+};
+
+// Arguments of a calibration launch: quantise an fp32 state into codes/scales.
+struct CalibArgs {
+  const float* S;        // [n][dv][dk]
+  uint8_t* codes;
+  float* scales;
+  float* ref;            // copy of S for the yoked policy, else null
+  int32_t n_heads, dv, group, ng;
+  int32_t nit, waves_per_head, total_waves;
+};
+
+// Launch geometry shared by the host and the kernels.
+struct Geometry {
+  int32_t lanes_per_row;   // lanes covering one state row
+  int32_t rows_per_iter;   // rows one wave covers per iteration (64 / lanes_per_row)
+};
+
+Geometry geometry(int bits, int dk);
+
+// Launchers.  Each returns hipErrorInvalidValue when no kernel instance
+// matches (the host API checks support before calling).
+hipError_t launch_step_q4(const StepArgs& a, int dk, int policy, int rounding, int delta, int diag,
+                          hipStream_t s);
+hipError_t launch_step_q8(const StepArgs& a, int dk, int policy, int rounding, int delta, int diag,
+                          hipStream_t s);
+hipError_t launch_step_f32(const StepArgs& a, int dk, int delta, int diag, hipStream_t s);
+hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace lsq

@@ -1,0 +1,183 @@
+// fp32-state decode step (the unquantised mode and the FP32-state baseline),
+// calibration of an fp32 state into a quantised handle, and the zero fill.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsq_step_impl.h"
+
+namespace lsq {
+
+Geometry geometry(int bits, int dk) {
+  Geometry g{};
+  if (bits == 32) {
+    g.lanes_per_row = 4;                 // interleaved fp32 layout, see step_f32_kernel
+  } else {
+    const int epl = 128 / bits;
+    g.lanes_per_row = dk / epl;
+  }
+  g.rows_per_iter = 64 / g.lanes_per_row;
+  return g;
+}
+
+namespace dev {
+
+// fp32 state.  Four lanes cover a row; lane lc owns the float4 chunks at
+// columns 16j + 4lc .. 16j + 4lc + 3 (j = 0 .. DK/16-1), so each load
+// instruction reads 64 contiguous bytes of every row the wave touches.
+// Arithmetic is Eq. (1) in the same fp32 order as the quantised kernels:
+// S' = fl(S * alpha_c), u = S'.k, w = fl(beta fl(v - u)), S = fma(w, k, S').
+template <int DK, int DELTA, int DIAG>
+__global__ __launch_bounds__(256) void step_f32_kernel(StepArgs a) {
+  constexpr int LPR = 4, RPI = 16, NC = DK / 16, EPL = DK / 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= a.total_waves) return;
+  const int h = wave / a.waves_per_head;
+  const int slice = wave - h * a.waves_per_head;
+  const int lr = lane / LPR, lc = lane % LPR;
+
+  float kk[EPL], qq[EPL], aa[DIAG ? EPL : 4];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = 16 * j + 4 * lc;
+    const float4 k4 = *reinterpret_cast<const float4*>(a.k + (size_t)h * DK + c);
+    const float4 q4 = *reinterpret_cast<const float4*>(a.q + (size_t)h * DK + c);
+    kk[4 * j] = k4.x; kk[4 * j + 1] = k4.y; kk[4 * j + 2] = k4.z; kk[4 * j + 3] = k4.w;
+    qq[4 * j] = q4.x; qq[4 * j + 1] = q4.y; qq[4 * j + 2] = q4.z; qq[4 * j + 3] = q4.w;
+    if constexpr (DIAG) {
+      const float4 a4 = *reinterpret_cast<const float4*>(a.alpha + (size_t)h * DK + c);
+      aa[4 * j] = a4.x; aa[4 * j + 1] = a4.y; aa[4 * j + 2] = a4.z; aa[4 * j + 3] = a4.w;
+    }
+  }
+  const float alpha_s = DIAG ? 1.f : a.alpha[h];
+  const float beta = a.beta[h];
+
+  for (int it = 0; it < a.nit; ++it) {
+    const int r = (slice * a.nit + it) * RPI + lr;
+    const bool live = r < a.dv;
+    const size_t row = (size_t)h * a.dv + (live ? r : a.dv - 1);
+    float* srow = a.ref + row * DK;
+    float sp[EPL];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const float4 x = *reinterpret_cast<const float4*>(srow + 16 * j + 4 * lc);
+      sp[4 * j] = x.x; sp[4 * j + 1] = x.y; sp[4 * j + 2] = x.z; sp[4 * j + 3] = x.w;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sp[e] = sp[e] * (DIAG ? aa[e] : alpha_s);
+    float u = 0.f;
+    if constexpr (DELTA) {
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p = fmaf(sp[e], kk[e], p);
+      u = row_sum<LPR>(p);
+    }
+    const float w = beta * (a.v[row] - u);
+    float po = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      sp[e] = fmaf(w, kk[e], sp[e]);
+      po = fmaf(sp[e], qq[e], po);
+    }
+    const float o = row_sum<LPR>(po);
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        *reinterpret_cast<float4*>(srow + 16 * j + 4 * lc) =
+            make_float4(sp[4 * j], sp[4 * j + 1], sp[4 * j + 2], sp[4 * j + 3]);
+      if (lc == 0) a.o[row] = o;
+    }
+  }
+}
+
+// Quantise an fp32 state: absmax group scale, round-half-even codes, clamp.
+template <int BITS, int DK>
+__global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
+  constexpr int EPL = 128 / BITS, LPR = DK / EPL, RPI = 64 / LPR, ROWB = DK * BITS / 8;
+  constexpr float QMAX = float((1 << (BITS - 1)) - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= a.total_waves) return;
+  const int h = wave / a.waves_per_head;
+  const int slice = wave - h * a.waves_per_head;
+  const int lr = lane / LPR, lc = lane % LPR, col0 = lc * EPL;
+  const int gl = a.group / EPL, gi = col0 / a.group;
+  for (int it = 0; it < a.nit; ++it) {
+    const int r = (slice * a.nit + it) * RPI + lr;
+    const bool live = r < a.dv;
+    const size_t row = (size_t)h * a.dv + (live ? r : a.dv - 1);
+    float x[EPL];
+    load_f32(x, a.S + row * DK + col0);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = group_max(amax, gl);
+    const float s = amax / QMAX;
+    const float inv = (s == 0.f) ? 0.f : 1.0f / s;
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float t = fmaf(x[e], inv, kMagic);
+      t = __builtin_amdgcn_fmed3f(t, kMagic - QMAX, kMagic + QMAX);
+      const uint32_t ci = static_cast<uint32_t>(static_cast<int>(t - kMagic));
+      if constexpr (BITS == 4)
+        out[e >> 3] |= (ci & 0xFu) << (4 * (e & 7));
+      else
+        out[e >> 2] |= (ci & 0xFFu) << (8 * (e & 3));
+    }
+    if (live) {
+      *reinterpret_cast<uint4*>(a.codes + row * ROWB + lc * 16) =
+          make_uint4(out[0], out[1], out[2], out[3]);
+      if ((lc % gl) == 0) a.scales[row * a.ng + gi] = s;
+      if (a.ref) store_f32(a.ref + row * DK + col0, x);
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(uint4* p, size_t n16, uint32_t* tail, size_t ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0u;
+}
+
+}  // namespace dev
+
+hipError_t launch_step_f32(const StepArgs& a, int dk, int delta, int diag, hipStream_t s) {
+  const dim3 grid((a.total_waves + 3) / 4), block(256);
+#define LSQ_F32(DK, D, G)                                                               \
+  if (dk == DK && delta == D && diag == G) {                                            \
+    hipLaunchKernelGGL((dev::step_f32_kernel<DK, D, G>), grid, block, 0, s, a);         \
+    return hipGetLastError();                                                           \
+  }
+  LSQ_F32(128, 0, 0) LSQ_F32(128, 0, 1) LSQ_F32(128, 1, 0) LSQ_F32(128, 1, 1)
+  LSQ_F32(64, 0, 0) LSQ_F32(64, 0, 1) LSQ_F32(64, 1, 0) LSQ_F32(64, 1, 1)
+#undef LSQ_F32
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s) {
+  const dim3 grid((a.total_waves + 3) / 4), block(256);
+#define LSQ_CAL(B, DK)                                                                  \
+  if (bits == B && dk == DK) {                                                          \
+    hipLaunchKernelGGL((dev::calibrate_kernel<B, DK>), grid, block, 0, s, a);           \
+    return hipGetLastError();                                                           \
+  }
+  LSQ_CAL(4, 128) LSQ_CAL(4, 64) LSQ_CAL(8, 128) LSQ_CAL(8, 64)
+#undef LSQ_CAL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16, ntail = (bytes % 16) / 4;
+  uint32_t* tail = reinterpret_cast<uint32_t*>(static_cast<char*>(p) + n16 * 16);
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(dev::fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<uint4*>(p), n16, tail, ntail);
+  return hipGetLastError();
+}
+
+}  // namespace lsq

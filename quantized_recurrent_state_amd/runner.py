@@ -1,0 +1,53 @@
+"""Workload set-up around the C ABI: handles, fp32 warmup, calibration, inputs.
+
+Step t of a workload uses the inputs drawn for step index t; a persistent
+workload first runs W unquantised (fp32) steps from S_0 = 0 (step indices
+0..W-1), freezes the group scales of S_W (lsq_state_calibrate) and then runs
+its quantised steps from index W.  This is the persistent-scale set-up of the
+workloads ("fixed from absmax of the fp32 state after a 64-step unquantized
+warmup"); every other workload starts quantised from S_0 = 0.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import LsqConfig, LsqState, POLICY_NONE, POLICY_PERSISTENT, ROUND_RNE
+from .inputs import Arm, Workload, gen_steps
+
+
+def arm_config(wl: Workload, arm: Arm, heads_per_layer: int | None = None) -> LsqConfig:
+    d = wl.arm_config(arm)
+    if heads_per_layer is not None:          # reduced copy for tests
+        d["batch"], d["heads"] = heads_per_layer * len(arm.layers), 1
+    return LsqConfig(**d)
+
+
+def fp32_config(cfg: LsqConfig) -> LsqConfig:
+    return LsqConfig(cfg.batch, cfg.heads, cfg.dk, cfg.dv, 32, 1, POLICY_NONE, ROUND_RNE,
+                     cfg.delta, cfg.decay)
+
+
+def inputs(wl: Workload, arm: Arm, t0: int, steps: int, n_per_layer: int, device) -> dict:
+    """Inputs of steps [t0, t0+steps) for this arm's layers (seed = layer index)."""
+    return gen_steps(wl.recipe, n_per_layer, wl.dk, wl.dv, arm.layers, t0, steps, device=device)
+
+
+def prepare(wl: Workload, arm: Arm, device, n_per_layer: int | None = None, chunk: int = 8,
+            keep_fp32: bool = False):
+    """Create the arm's handle at S_0 = 0 and, for a persistent arm, run the fp32
+    warmup and calibrate.  Returns (state, first quantised step index, S_W or None)."""
+    npl = n_per_layer if n_per_layer is not None else wl.batch * wl.heads
+    cfg = arm_config(wl, arm, None if n_per_layer is None else npl)
+    st = LsqState(cfg, device=device).zero()
+    if arm.policy != POLICY_PERSISTENT or wl.warmup == 0:
+        return st, 0, None
+    f = LsqState(fp32_config(cfg), device=device).zero()
+    for t0 in range(0, wl.warmup, chunk):
+        n = min(chunk, wl.warmup - t0)
+        d = inputs(wl, arm, t0, n, npl, device)
+        f.run(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        del d
+    st.calibrate(f.f32)
+    S_W = f.f32 if keep_fp32 else None
+    del f
+    return st, wl.warmup, S_W

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library loads, exports every function include/lsq.h declares, sizes the
+state buffers as the packed layout defines, and rejects bad arguments with the
+documented status before touching the device.  The device pointers used here
+are never dereferenced: every call below fails validation (or is a no-op)
+before any launch.
+"""
+import ctypes
+
+import pytest
+
+import quantized_recurrent_state_amd as lsq
+from quantized_recurrent_state_amd import _lib
+
+FAKE = 0x7F0000000000          # a 16-byte aligned address that is never touched
+
+
+def test_every_declared_symbol_is_exported():
+    L = _lib.load()
+    names = _lib.header_functions()
+    assert {"lsq_state_alloc", "lsq_decode_step", "lsq_decode_run"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert lsq.lsq_version() >= 100
+
+
+@pytest.mark.parametrize("cfg,want", [
+    # INT4 g32 128x128: 64 B codes + 4 scales per row
+    (lsq.LsqConfig(2, 3, 128, 128, 4, 32, lsq.POLICY_PERSISTENT), (6 * 128 * 64, 6 * 128 * 16, 0, 0)),
+    # INT8 g64 Dv 64: 128 B codes + 2 scales per row
+    (lsq.LsqConfig(1, 5, 128, 64, 8, 64, lsq.POLICY_DYNAMIC), (5 * 64 * 128, 5 * 64 * 8, 0, 0)),
+    # yoked adds the fp32 reference
+    (lsq.LsqConfig(1, 1, 64, 64, 4, 32, lsq.POLICY_YOKED), (64 * 32, 64 * 8, 64 * 64 * 4, 0)),
+    # fp32 state
+    (lsq.LsqConfig(1, 2, 64, 32, 32, 1, lsq.POLICY_NONE), (0, 0, 0, 2 * 32 * 64 * 4)),
+])
+def test_state_sizes(cfg, want):
+    assert lsq.lsq_state_sizes(cfg) == want
+
+
+BAD = [
+    (dict(bits=5), 1), (dict(bits=32, policy=lsq.POLICY_DYNAMIC), 1),
+    (dict(policy=lsq.POLICY_NONE), 1), (dict(group=48), 1), (dict(group=0), 1),
+    (dict(delta=2), 1), (dict(decay=3), 1), (dict(rounding=7), 1), (dict(batch=-1), 1),
+    (dict(dk=96, group=32), 2), (dict(group=16), 2), (dict(bits=8, group=8), 2),
+    (dict(dk=256, group=32), 2),
+]
+
+
+@pytest.mark.parametrize("change,status", BAD)
+def test_invalid_configs_are_rejected(change, status):
+    base = dict(batch=1, heads=1, dk=128, dv=128, bits=4, group=32,
+                policy=lsq.POLICY_PERSISTENT, rounding=0, delta=0, decay=0)
+    base.update(change)
+    cfg = lsq.LsqConfig(**base)
+    with pytest.raises(lsq.LsqError) as e:
+        lsq.lsq_state_sizes(cfg)
+    assert e.value.status == status
+    assert _lib.load().lsq_last_error().decode() != ""
+
+
+def _alloc(cfg, codes=FAKE, cb=None, scales=FAKE, sb=None):
+    L = _lib.load()
+    need = lsq.lsq_state_sizes(cfg)
+    bufs = _lib.lsq_buffers(codes, need[0] if cb is None else cb, scales,
+                            need[1] if sb is None else sb, None, 0, None, 0)
+    h = ctypes.c_void_p()
+    st = L.lsq_state_alloc(ctypes.byref(cfg.c()), ctypes.byref(bufs), ctypes.byref(h))
+    return st, h.value
+
+
+def test_alloc_checks_buffers():
+    cfg = lsq.LsqConfig(1, 2, 128, 16, 4, 32, lsq.POLICY_PERSISTENT)
+    assert _alloc(cfg, codes=None)[0] == 1
+    assert _alloc(cfg, codes=FAKE + 8)[0] == 1                 # misaligned
+    assert _alloc(cfg, cb=100)[0] == 3                         # too small
+    st, h = _alloc(cfg)
+    assert st == 0 and h
+    out = _lib.lsq_config()
+    assert _lib.load().lsq_state_config(h, ctypes.byref(out)) == 0 and out.dk == 128
+    lsq.lsq_state_free(h)
+    lsq.lsq_state_free(None)                                   # no-op
+
+
+def test_step_argument_checks_before_launch():
+    L = _lib.load()
+    cfg = lsq.LsqConfig(1, 2, 128, 16, 4, 32, lsq.POLICY_PERSISTENT)
+    st, h = _alloc(cfg)
+    assert st == 0
+    ptrs = [FAKE] * 6
+    # persistent policy without calibration
+    assert L.lsq_decode_step(h, *ptrs, None, None) == 4
+    assert L.lsq_decode_run(h, 3, *ptrs, None, None) == 4
+    assert L.lsq_state_set_calibrated(h, 1) == 0
+    # null and misaligned inputs
+    assert L.lsq_decode_step(h, None, *ptrs[1:], None, None) == 1
+    assert L.lsq_decode_step(h, FAKE + 4, *ptrs[1:], None, None) == 1
+    assert L.lsq_decode_run(h, -1, *ptrs, None, None) == 1
+    assert L.lsq_decode_run(h, 0, *ptrs, None, None) == 0       # empty horizon
+    assert L.lsq_decode_step(None, *ptrs, None, None) == 1
+    lsq.lsq_state_free(h)
+
+
+def test_empty_batch_calls_are_noops():
+    L = _lib.load()
+    cfg = lsq.LsqConfig(0, 4, 128, 128, 4, 32, lsq.POLICY_DYNAMIC)
+    st, h = _alloc(cfg, codes=None, scales=None)
+    assert st == 0
+    assert L.lsq_decode_step(h, None, None, None, None, None, None, None, None) == 0
+    assert L.lsq_state_calibrate(h, None, None) == 0
+    lsq.lsq_state_free(h)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert lsq.lsq_status_string(s).startswith(_lib.STATUS_NAMES[s])

@@ -1,0 +1,170 @@
+"""GPU parity: the HIP decode step against the CPU oracle, element by element.
+
+Every flag combination (bits, Dk, policy, rounding, delta, decay) runs a few
+steps on small states whose Dv leaves a ragged tail of rows and whose head
+count leaves a partially filled last workgroup; every step is compared
+teacher-forced (tests/parity.py states the bar).  The fp32-state mode is
+compared free-running over a whole horizon.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_recurrent_state_amd as lsq
+from quantized_recurrent_state_amd.inputs import gen_steps
+from tests.parity import Report, compare_step, ocfg_of, snapshot, _normwise
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _inputs(recipe, n, dk, dv, t0, steps, seed=0):
+    d = gen_steps(recipe, n, dk, dv, [seed], t0, steps, device="cpu")
+    return {k: v.to(DEV) for k, v in d.items()}, {k: v.numpy() for k, v in d.items()}
+
+
+def _np_step(d, t):
+    return (d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t])
+
+
+def _run_teacher_forced(cfg, steps, recipe, warmup=4):
+    """Run the GPU path, comparing each step with the oracle from the GPU's state."""
+    ocfg = ocfg_of(cfg)
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    rep = Report()
+    t0 = 0
+    if cfg.policy == lsq.POLICY_PERSISTENT:
+        f = lsq.LsqState(lsq.LsqConfig(cfg.batch, cfg.heads, cfg.dk, cfg.dv, 32, 1,
+                                       lsq.POLICY_NONE, 0, cfg.delta, cfg.decay), device=DEV).zero()
+        dg, _ = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, 0, warmup)
+        f.run(dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"])
+        st.calibrate(f.f32)
+        # calibration itself: bit-exact against the oracle's quantiser
+        want = oracle.calibrate(ocfg, f.f32.cpu().numpy())
+        got = snapshot(st)
+        assert np.array_equal(got.codes, want.codes)
+        assert np.array_equal(got.scales, want.scales)
+        t0 = warmup
+    dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, t0, steps)
+    before = snapshot(st)
+    for t in range(steps):
+        out = st.step(dg["q"][t], dg["k"][t], dg["v"][t], dg["alpha"][t], dg["beta"][t])
+        o, o_ref = out if cfg.policy == lsq.POLICY_YOKED else (out, None)
+        after = snapshot(st)
+        rep.add(compare_step(ocfg, before, _np_step(dn, t), after, o.cpu().numpy(),
+                             None if o_ref is None else o_ref.cpu().numpy()))
+        before = after
+    return rep
+
+
+COMBOS = [(bits, dk, pol, rnd, dl, dc)
+          for bits in (4, 8)
+          for dk in (128, 64)
+          for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT, lsq.POLICY_YOKED)
+          for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+          for dl in (0, 1)
+          for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc", COMBOS)
+def test_step_matches_oracle(bits, dk, pol, rnd, dl, dc):
+    group = 32 if bits == 4 else 64
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=44, bits=bits, group=min(group, dk),
+                        policy=pol, rounding=rnd, delta=dl, decay=dc)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=6, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (4, 128), (8, 16), (8, 32), (8, 128)])
+def test_other_group_sizes(bits, group):
+    for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT):
+        cfg = lsq.LsqConfig(batch=1, heads=5, dk=128, dv=24, bits=bits, group=group, policy=pol,
+                            rounding=lsq.ROUND_BDR, delta=1, decay=0)
+        rep = _run_teacher_forced(cfg, steps=4, recipe="gdn")
+        assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+@pytest.mark.parametrize("dl,dc", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fp32_state_free_running(dk, dl, dc):
+    """Unquantised mode over a whole horizon: S_H and every o_t within 1e-5."""
+    cfg = lsq.LsqConfig(batch=3, heads=2, dk=dk, dv=37, bits=32, group=1,
+                        policy=lsq.POLICY_NONE, rounding=0, delta=dl, decay=dc)
+    H = 40
+    recipe = "gla" if dc else ("gdn" if dl else "mamba2")
+    dg, dn = _inputs(recipe, cfg.n, dk, cfg.dv, 0, H)
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    o = st.run(dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"])
+    ost = oracle.zero_state(ocfg_of(cfg))
+    oo, _ = oracle.run(ocfg_of(cfg), ost, dn["q"], dn["k"], dn["v"], dn["alpha"], dn["beta"])
+    assert _normwise(st.f32.cpu().numpy(), ost.f32) <= 1e-5
+    for t in range(H):
+        assert _normwise(o[t].cpu().numpy(), oo[t]) <= 1e-5, t
+
+
+def test_run_equals_repeated_steps_and_is_deterministic():
+    cfg = lsq.LsqConfig(batch=4, heads=4, dk=128, dv=128, bits=4, group=32,
+                        policy=lsq.POLICY_DYNAMIC, rounding=lsq.ROUND_BDR, delta=1, decay=0)
+    dg, _ = _inputs("gdn", cfg.n, 128, 128, 0, 10)
+    a = lsq.LsqState(cfg, device=DEV).zero()
+    b = lsq.LsqState(cfg, device=DEV).zero()
+    c = lsq.LsqState(cfg, device=DEV).zero()
+    oa = a.run(dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"])
+    ob = torch.stack([b.step(dg["q"][t], dg["k"][t], dg["v"][t], dg["alpha"][t], dg["beta"][t])
+                      for t in range(10)])
+    oc = c.run(dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"])
+    for x, y in ((a, b), (a, c)):
+        assert torch.equal(x.codes, y.codes) and torch.equal(x.scales, y.scales)
+    assert torch.equal(oa, ob) and torch.equal(oa, oc)
+
+
+def test_checkpoint_resume_is_bit_identical():
+    """A copy of the state buffers bound to a new handle resumes exactly."""
+    cfg = lsq.LsqConfig(batch=2, heads=8, dk=128, dv=128, bits=4, group=32,
+                        policy=lsq.POLICY_PERSISTENT, rounding=lsq.ROUND_BDR, delta=1, decay=0)
+    dg, _ = _inputs("gdn", cfg.n, 128, 128, 0, 12)
+    S0 = torch.randn(cfg.n, 128, 128, device=DEV) * 0.1
+    a = lsq.LsqState(cfg, device=DEV).zero().calibrate(S0)
+    a.run(*(dg[x][:6] for x in ("q", "k", "v", "alpha", "beta")))
+    b = lsq.LsqState(cfg, device=DEV)
+    b.codes.copy_(a.codes)
+    b.scales.copy_(a.scales)
+    with pytest.raises(lsq.LsqError, match="NOT_CALIBRATED"):
+        b.step(dg["q"][6], dg["k"][6], dg["v"][6], dg["alpha"][6], dg["beta"][6])
+    b.set_calibrated(True)
+    oa = a.run(*(dg[x][6:] for x in ("q", "k", "v", "alpha", "beta")))
+    ob = b.run(*(dg[x][6:] for x in ("q", "k", "v", "alpha", "beta")))
+    assert torch.equal(oa, ob) and torch.equal(a.codes, b.codes)
+
+
+def test_edge_cases():
+    # empty batch: steps are no-ops
+    cfg = lsq.LsqConfig(batch=0, heads=4, dk=128, dv=128, bits=4, group=32,
+                        policy=lsq.POLICY_DYNAMIC)
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    z = torch.zeros(0, 128, device=DEV)
+    st.step(z, z, z, torch.zeros(0, device=DEV), torch.zeros(0, device=DEV))
+    # a single row, one group spanning the whole row, zero inputs keep S = 0
+    cfg = lsq.LsqConfig(batch=1, heads=3, dk=128, dv=1, bits=8, group=128,
+                        policy=lsq.POLICY_DYNAMIC, rounding=lsq.ROUND_BDR, delta=1)
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    zq = torch.zeros(3, 128, device=DEV)
+    o = st.step(zq, zq, torch.zeros(3, 1, device=DEV), torch.ones(3, device=DEV),
+                torch.ones(3, device=DEV))
+    assert torch.count_nonzero(st.codes) == 0 and torch.count_nonzero(o) == 0
+    assert torch.count_nonzero(st.scales) == 0
+    # saturation: a persistent scale far too small clamps every written element
+    cfg = lsq.LsqConfig(batch=1, heads=2, dk=128, dv=16, bits=4, group=32,
+                        policy=lsq.POLICY_PERSISTENT, rounding=lsq.ROUND_BDR, delta=0)
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    st.calibrate(torch.full((2, 16, 128), 1e-6, device=DEV))
+    k = torch.ones(2, 128, device=DEV)
+    st.step(k, k, torch.full((2, 16), 1e3, device=DEV), torch.ones(2, device=DEV),
+            torch.ones(2, device=DEV))
+    codes = oracle.unpack(st.codes.cpu().numpy(), 4, 128)
+    assert np.all(codes == 7)
