@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: one JSON line on stdout.
+
+A "step" is one decode step of the whole workload (every arm / bit-width
+segment, every head) over one batch of synthetic inputs already resident in
+HBM.  The default workload is the long-horizon mixed-precision stack: 24
+independent Gated-DeltaNet layers x batch 512 x 32 heads, Dk = Dv = 128,
+delta rule, persistent scales after a 64-step fp32 warmup, bounded
+directional rounding; layers 0-3 INT8 g64, layers 4-23 INT4 g32 (two launches
+per step).
+
+value       algorithmic state-update bytes per step x steps / wall time (GB/s)
+roofline    the dominant kernel (the INT4 g32 segment): its algorithmic bytes
+            per launch / its mean launch time from HIP events recorded around
+            each launch on the launch stream, against 8 TB/s; traffic = HBM
+            bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (profiles/),
+            reported only while the kernel sources match the profiled ones
+cpu_baseline  the CPU oracle on a bounded sample of the same workload (sampled
+            heads, a few steps, the host threads stated), in the same unit
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "state-update HBM GB/s (% of peak) and batch·head·steps/s, INT4 g32"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("quantized_recurrent_state_amd/csrc/lsq_step_impl.h",
+                  "quantized_recurrent_state_amd/csrc/lsq_step_q4.hip",
+                  "quantized_recurrent_state_amd/csrc/lsq_step_q8.hip")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stack24")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--fp32-steps", type=int, default=8,
+                    help="steps of the fp32-state comparison run (0 disables it)")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures the decode step on one GPU only; the step needs "
+              "no exchange between GPUs, and runs with --gpus above 1 are not part of it",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import quantized_recurrent_state_amd as lsq
+    from quantized_recurrent_state_amd import runner
+    from quantized_recurrent_state_amd.inputs import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    stream = torch.cuda.current_stream()
+
+    # ---- set-up (untimed): handles, fp32 warmup + calibration, resident inputs
+    arms = []
+    shared = None
+    t_setup = time.perf_counter()
+    for arm in wl.arms:
+        st, t_first, _ = runner.prepare(wl, arm, dev)
+        cfg = st.cfg
+        npl = wl.batch * wl.heads
+        if wl.shared_inputs and shared is not None:
+            inp = shared
+        else:
+            inp = runner.inputs(wl, arm, t_first, W + K, npl, dev)
+            if wl.shared_inputs:
+                shared = inp
+        o = torch.empty((cfg.n, cfg.dv), device=dev)
+        o_ref = torch.empty((cfg.n, cfg.dv), device=dev) if cfg.policy == lsq.POLICY_YOKED else None
+        arms.append(dict(arm=arm, st=st, cfg=cfg, inp=inp, o=o, o_ref=o_ref,
+                         bytes=runner.algorithmic_bytes(cfg, o_ref is not None)))
+        log(f"arm {arm.name}: {cfg} bytes/step {arms[-1]['bytes'] / 1e9:.3f} GB")
+    torch.cuda.synchronize()
+    log(f"set-up {time.perf_counter() - t_setup:.1f} s")
+    dom = max(range(len(arms)), key=lambda i: arms[i]["bytes"])
+
+    def launch(a, t):
+        i = a["inp"]
+        lsq.lsq_decode_step(a["st"].handle, i["q"][t], i["k"][t], i["v"][t], i["alpha"][t],
+                            i["beta"][t], a["o"], a["o_ref"], stream)
+
+    for t in range(W):
+        for a in arms:
+            launch(a, t)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events around every launch of the dominant kernel
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j, t in enumerate(range(W, W + K)):
+        for i, a in enumerate(arms):
+            if i == dom:
+                ev_s[j].record(stream)
+            launch(a, t)
+            if i == dom:
+                ev_e[j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(ev_s, ev_e)]
+    kern_ms_mean = sum(kern_ms) / len(kern_ms)
+
+    bytes_step = sum(a["bytes"] for a in arms)
+    heads_step = sum(a["cfg"].n for a in arms)
+    gbs = bytes_step * K / wall / 1e9
+    dom_a = arms[dom]
+    dom_gbs = dom_a["bytes"] / (kern_ms_mean * 1e-3) / 1e9
+    log(f"timed {K} steps: {wall * 1e3 / K:.3f} ms/step, {gbs:.1f} GB/s; dominant kernel "
+        f"{kern_ms_mean * 1e3:.1f} us, {dom_gbs:.1f} GB/s")
+
+    traffic = None
+    sha = kernel_source_sha()
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if (tr.get("source_sha") == sha and tr.get("workload") == wl.name
+                and tr.get("arm") == dom_a["arm"].name):
+            traffic = int(tr["hbm_bytes_per_launch"])
+
+    # ---- copy probe for counter calibration (outside the timed region)
+    if args.copy_probe_gib > 0:
+        nb = int(args.copy_probe_gib * (1 << 30)) // 4
+        src = torch.ones(nb, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {nb * 4} bytes read and written")
+        del src, dst
+
+    # ---- fp32-state comparison at the same shapes (the 'vs FP32 states' context)
+    fp32 = None
+    if args.fp32_steps > 0:
+        fl = []
+        for a in arms:
+            f = lsq.LsqState(runner.fp32_config(a["cfg"]), device=dev).zero()
+            fl.append((a, f))
+        torch.cuda.synchronize()
+        nf = min(args.fp32_steps, W + K)
+        tf0 = time.perf_counter()
+        for t in range(nf):
+            for a, f in fl:
+                i = a["inp"]
+                lsq.lsq_decode_step(f.handle, i["q"][t], i["k"][t], i["v"][t], i["alpha"][t],
+                                    i["beta"][t], a["o"], None, stream)
+        torch.cuda.synchronize()
+        fms = (time.perf_counter() - tf0) * 1e3 / nf
+        fbytes = sum(runner.algorithmic_bytes(f.cfg) for _, f in fl)
+        fp32 = {"ms_per_step": round(fms, 4), "state_bytes_per_step": fbytes,
+                "speedup_of_quantised_step": round(fms / (wall * 1e3 / K), 3),
+                "state_memory_ratio": round(
+                    sum(f.f32.numel() * 4 for _, f in fl)
+                    / sum(a["st"].codes.numel() + a["st"].scales.numel() * 4 for a in arms), 3)}
+        del fl
+        log(f"fp32-state step {fms:.3f} ms")
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(arms, args.cpu_seconds, W + K)
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "head_steps_per_s": round(heads_step * K / wall, 1),
+        "config": {"workload": wl.name, "layers": sum(len(a["arm"].layers) for a in arms),
+                   "batch_per_layer": wl.batch, "heads": wl.heads, "dk": wl.dk, "dv": wl.dv,
+                   "delta": wl.delta, "decay": "diag" if wl.decay else "scalar",
+                   "arms": [{"name": a["arm"].name, "bits": a["cfg"].bits,
+                             "group": a["cfg"].group, "policy": a["cfg"].policy,
+                             "rounding": a["cfg"].rounding, "heads": a["cfg"].n,
+                             "bytes_per_step": a["bytes"]} for a in arms],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": f"decode step, {dom_a['arm'].name}",
+                     "algorithmic_bytes_per_launch": dom_a["bytes"],
+                     "launch_us_mean": round(kern_ms_mean * 1e3, 2),
+                     "launch_us_min": round(min(kern_ms) * 1e3, 2),
+                     "source_sha": sha},
+        "fp32_state": fp32,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(arms, seconds: float, steps_avail: int):
+    """Time the CPU oracle on sampled heads of every arm (same inputs and state
+    as the GPU), scaled to the benchmark's unit."""
+    import numpy as np
+    import oracle
+    from quantized_recurrent_state_amd import runner
+    from tests.parity import ocfg_of, snapshot
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    frac = 1.0 / 32                               # sampled share of every arm's heads
+    samples = []
+    for a in arms:
+        n = a["cfg"].n
+        m = max(threads, int(n * frac))
+        idx = np.linspace(0, n - 1, m).astype(np.int64)
+        sel = __import__("torch").as_tensor(idx, device=a["st"].device)
+        st = snapshot(a["st"], heads=sel)
+        ocfg = ocfg_of(a["cfg"]).replace(batch=m, heads=1)
+        samples.append((a, ocfg, st, sel))
+
+    def run(steps):
+        total_b, total_hs, dt = 0, 0, 0.0
+        for a, ocfg, st, sel in samples:
+            i = a["inp"]
+            x = {k: i[k][:steps].index_select(1, sel).cpu().numpy() for k in i}
+            s2 = st.copy()
+            t0 = time.perf_counter()
+            oracle.run(ocfg, s2, x["q"], x["k"], x["v"], x["alpha"], x["beta"], nthreads=threads)
+            dt += time.perf_counter() - t0
+            total_b += runner.algorithmic_bytes(a["cfg"]) // a["cfg"].n * ocfg.n * steps
+            total_hs += ocfg.n * steps
+        return total_b, total_hs, dt
+
+    _, _, dt1 = run(1)
+    steps = int(max(1, min(steps_avail, round(seconds / max(dt1, 1e-3)))))
+    b, hs, dt = run(steps)
+    heads = sum(o.n for _, o, _, _ in samples)
+    log(f"cpu oracle: {heads} sampled heads x {steps} steps in {dt:.1f} s on {threads} threads")
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "head_steps_per_s": round(hs / dt, 1),
+            "sample": f"{heads} heads (1/32 of every arm, evenly spaced) x {steps} steps of the "
+                      f"same workload, from the GPU's state, on the same inputs"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -47,7 +47,9 @@
  * Packed state layout (per handle, heads = batch*heads):
  *   codes  [heads][Dv][Dk*bits/8] bytes.  INT8: one two's-complement byte per
  *          element.  INT4: element c of a row in byte c/2, low nibble for even
- *          c, two's-complement nibble.  Codes lie in [-qmax, qmax].
+ *          c, two's-complement nibble.  Codes lie in [-qmax, qmax]; the
+ *          most negative code (-8, -128) is never produced and is not a
+ *          valid input.
  *   scales [heads][Dv][Dk/group] fp32, one per contiguous group along Dk.
  *   ref    [heads][Dv][Dk] fp32, the yoked policy's reference state.
  *   f32    [heads][Dv][Dk] fp32, the state of the unquantised mode (bits 32).
@@ -60,8 +62,9 @@
  * happen on the host before any launch and return a status without touching
  * the device.  Launch failures return LSQ_ERR_HIP.  No C++ exception crosses
  * the ABI.  A handle must not be used on two streams at once.  Inputs must be
- * finite; the data is not scanned.  With batch*heads == 0 every call is a
- * no-op and its data pointers may be NULL.
+ * finite and the state far from overflow (scales and |S| below 2^100); the
+ * data is not scanned.  With batch*heads == 0 every call is a no-op and its
+ * data pointers may be NULL.
  */
 #ifndef LSQ_H
 #define LSQ_H
@@ -95,8 +98,8 @@ typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
 /* Shape, format and method flags of one handle.
  *   bits   4, 8 (quantised) or 32 (fp32 state, policy NONE)
  *   group  group size along Dk; must divide dk.  This build supports
- *          INT4 groups of 32/64/128 and INT8 groups of 16/32/64/128 (a group
- *          never smaller than the 16 bytes one lane owns), Dk in {64, 128}.
+ *          power-of-two groups of 32 to Dk elements (one lane owns 32
+ *          consecutive elements of a row) and Dk in {64, 128}.
  *   delta  0: linear write, 1: delta-rule correction
  */
 typedef struct {

@@ -9,12 +9,10 @@ namespace lsq {
 
 Geometry geometry(int bits, int dk) {
   Geometry g{};
-  if (bits == 32) {
+  if (bits == 32)
     g.lanes_per_row = 4;                 // interleaved fp32 layout, see step_f32_kernel
-  } else {
-    const int epl = 128 / bits;
-    g.lanes_per_row = dk / epl;
-  }
+  else
+    g.lanes_per_row = dk / dev::EPL;     // 32 elements per lane
   g.rows_per_iter = 64 / g.lanes_per_row;
   return g;
 }
@@ -91,10 +89,11 @@ __global__ __launch_bounds__(256) void step_f32_kernel(StepArgs a) {
 }
 
 // Quantise an fp32 state: absmax group scale, round-half-even codes, clamp.
+// Same lane layout as the step kernels (32 elements per lane).
 template <int BITS, int DK>
 __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
-  constexpr int EPL = 128 / BITS, LPR = DK / EPL, RPI = 64 / LPR, ROWB = DK * BITS / 8;
-  constexpr float QMAX = float((1 << (BITS - 1)) - 1);
+  using F = Fmt<BITS>;
+  constexpr int LPR = DK / EPL, RPI = 64 / LPR, ROWB = DK * BITS / 8;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wave >= a.total_waves) return;
@@ -112,22 +111,20 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
     amax = group_max(amax, gl);
-    const float s = amax / QMAX;
+    const float s = amax / F::QMAX;
     const float inv = (s == 0.f) ? 0.f : 1.0f / s;
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    float t[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float t = fmaf(x[e], inv, kMagic);
-      t = __builtin_amdgcn_fmed3f(t, kMagic - QMAX, kMagic + QMAX);
-      const uint32_t ci = static_cast<uint32_t>(static_cast<int>(t - kMagic));
-      if constexpr (BITS == 4)
-        out[e >> 3] |= (ci & 0xFu) << (4 * (e & 7));
-      else
-        out[e >> 2] |= (ci & 0xFFu) << (8 * (e & 3));
-    }
+    for (int e = 0; e < EPL; ++e)
+      t[e] = __builtin_amdgcn_fmed3f(fmaf(x[e], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
+    uint32_t X[F::NW];
+    pack_offsets<BITS>(t, X);
     if (live) {
-      *reinterpret_cast<uint4*>(a.codes + row * ROWB + lc * 16) =
-          make_uint4(out[0], out[1], out[2], out[3]);
+      uint8_t* p = a.codes + row * ROWB + lc * (EPL * BITS / 8);
+#pragma unroll
+      for (int c = 0; c < F::NW / 4; ++c)
+        reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c] ^ F::OFF, X[4 * c + 1] ^ F::OFF,
+                                                    X[4 * c + 2] ^ F::OFF, X[4 * c + 3] ^ F::OFF);
       if ((lc % gl) == 0) a.scales[row * a.ng + gi] = s;
       if (a.ref) store_f32(a.ref + row * DK + col0, x);
     }

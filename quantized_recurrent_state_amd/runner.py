@@ -51,3 +51,22 @@ def prepare(wl: Workload, arm: Arm, device, n_per_layer: int | None = None, chun
     S_W = f.f32 if keep_fp32 else None
     del f
     return st, wl.warmup, S_W
+
+
+def algorithmic_bytes(cfg: LsqConfig, with_o_ref: bool = False) -> int:
+    """Bytes one decode step must move for this handle (all heads): packed codes
+    read and written, group scales read (and written by the dynamic and yoked
+    policies), the yoked fp32 reference read and written, the step inputs
+    q, k, v, alpha, beta read and the output o (and o_ref) written."""
+    from . import POLICY_DYNAMIC, POLICY_YOKED, DECAY_DIAG
+    n, dk, dv = cfg.n, cfg.dk, cfg.dv
+    if cfg.bits == 32:
+        state = 2 * 4 * dv * dk
+    else:
+        state = 2 * dv * dk * cfg.bits // 8
+        state += dv * (dk // cfg.group) * 4 * (2 if cfg.policy in (POLICY_DYNAMIC, POLICY_YOKED) else 1)
+        if cfg.policy == POLICY_YOKED:
+            state += 2 * 4 * dv * dk
+    ins = 4 * (2 * dk + dv + (dk if cfg.decay == DECAY_DIAG else 1) + 1)
+    outs = 4 * dv * (2 if (with_o_ref and cfg.policy == POLICY_YOKED) else 1)
+    return n * (state + ins + outs)
