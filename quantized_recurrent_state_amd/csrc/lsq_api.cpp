@@ -8,7 +8,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/lsq.h"
+#include "lsq.h"
 #include "lsq_internal.h"
 
 struct lsq_state {

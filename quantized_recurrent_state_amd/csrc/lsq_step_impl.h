@@ -105,6 +105,14 @@ __device__ __forceinline__ void store_f32(float* __restrict__ dst, const float (
                                                     src[4 * i + 3]);
 }
 
+template <int N>
+__device__ __forceinline__ void store_lds(float* dst, const float (&src)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i)
+    reinterpret_cast<float4*>(dst)[i] = make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2],
+                                                    src[4 * i + 3]);
+}
+
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 
 // x & m, opaque to the optimiser: keeps "(w >> 8b) & 0xFF -> float" as one
@@ -211,6 +219,20 @@ __device__ __forceinline__ void pack_offsets(const float (&t)[EPL], uint32_t (&X
   }
 }
 
+// Eight rounded values (elements 8b..8b+7) -> the offset-binary word(s) they fill.
+template <int BITS>
+__device__ __forceinline__ void pack_block(const float (&t)[8], uint32_t* X) {
+  if constexpr (BITS == 4) {
+    uint32_t p[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) p[b] = (fbits(t[2 * b + 1]) << 4) | fbits(t[2 * b]);
+    X[0] = gather_low_bytes(p[0], p[1], p[2], p[3]);
+  } else {
+    X[0] = gather_low_bytes(fbits(t[0]), fbits(t[1]), fbits(t[2]), fbits(t[3]));
+    X[1] = gather_low_bytes(fbits(t[4]), fbits(t[5]), fbits(t[6]), fbits(t[7]));
+  }
+}
+
 // Per-lane row data, loaded one iteration ahead.
 template <int BITS>
 struct RowIn {
@@ -235,48 +257,292 @@ __device__ __forceinline__ void load_row(RowIn<BITS>& R, const StepArgs& a, size
   R.v = a.v[row];
 }
 
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG>
-__global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
+#ifndef LSQ_STEP_WAVES_PER_EU
+#define LSQ_STEP_WAVES_PER_EU 2
+#endif
+
+// Per-lane, per-head state of a wave: its place in the grid, the orientation
+// masks of its 32 columns, and where the head's vectors sit in LDS.  The
+// vectors (k, q, a diagonal decay; oriented for directional rounding) are
+// staged once per wave in LDS (3 KiB per wave at most) and read per row,
+// which keeps them out of the register file: more waves fit on a SIMD.
+constexpr int kVecs = 5;   // k, q, alpha, natural k, natural q
+template <int BITS, int POLICY, int ROUND, int DIAG>
+struct Lane {
+  static constexpr bool BDR = ROUND == RND_BDR;
+  static constexpr int NW = Fmt<BITS>::NW;
+  int h, slice, lr, lc, col0, gl, gi;
+  int vbase;          // float offset of this wave's vectors in the LDS array
+  float alpha_s, beta;
+  uint32_t Kf[BDR ? NW : 1], Kx[BDR ? NW : 1], K1[BDR ? NW : 1];
+};
+
+// Eight consecutive floats of an LDS vector, read with two 16-byte loads.
+// The row loop passes a base offset laundered through an empty asm once per
+// row, so that these reads stay inside the loop instead of being hoisted into
+// registers; the block offsets are constants (immediate ds_read offsets).
+template <int DK>
+__device__ __forceinline__ void lds_block(float (&d)[8], const float* lds, int off) {
+  const float4 a = *reinterpret_cast<const float4*>(lds + off);
+  const float4 b = *reinterpret_cast<const float4*>(lds + off + 4);
+  d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+  d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+}
+
+// The row loop of one wave.  KZ: the head's key has a zero component (no
+// update direction there), so those elements drop their round-up candidate.
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, bool KZ>
+__device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, ROUND, DIAG>& L,
+                                         const float* vec) {
+  // vec + L.vbase + v*DK + L.col0: this lane's 32 columns of vector v
+  const int base0 = L.vbase + L.col0;
   using F = Fmt<BITS>;
   constexpr int NW = F::NW;
   constexpr int LPR = DK / EPL;          // lanes per row
   constexpr int RPI = 64 / LPR;          // rows per wave-iteration
   constexpr int ROWB = DK * BITS / 8;    // packed bytes per row
+  constexpr int WPB = BITS == 4 ? 1 : 2; // code words per block of 8 elements
+  constexpr bool BDR = ROUND == RND_BDR;
+
+  const int it0 = L.slice * a.nit;
+  auto row_of = [&](int it, bool& live) {
+    const int r = (it0 + it) * RPI + L.lr;
+    live = r < a.dv;                     // uniform over the lanes of a row
+    return (size_t)L.h * a.dv + (live ? r : a.dv - 1);
+  };
+
+  RowIn<BITS> nxt;
+  bool live_n;
+  size_t row_n = row_of(0, live_n);
+  load_row<BITS, DK>(nxt, a, row_n, L.lc, L.gi);
+
+  for (int it = 0; it < a.nit; ++it) {
+    int base = base0;
+    asm volatile("" : "+v"(base));
+    const int kOff = base, qOff = base + DK, aOff = base + 2 * DK;
+    const int knOff = base + 3 * DK, qnOff = base + 4 * DK;
+    (void)qOff; (void)aOff; (void)knOff; (void)qnOff;
+    const RowIn<BITS> in = nxt;
+    const bool live = live_n;
+    const size_t row = row_n;
+    if (it + 1 < a.nit) {
+      row_n = row_of(it + 1, live_n);
+      load_row<BITS, DK>(nxt, a, row_n, L.lc, L.gi);
+    }
+    float R[POLICY == POL_YOKED ? EPL : 4];
+    float* rp = a.ref + row * DK + L.col0;
+    if constexpr (POLICY == POL_YOKED) load_f32(R, rp);
+
+    // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha))
+    uint32_t xo[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      if constexpr (BDR)
+        xo[j] = (in.x[j] ^ L.Kx[j]) + L.K1[j];   // offset code, negated where k_c < 0
+      else
+        xo[j] = in.x[j] ^ F::OFF;
+    }
+    float sp[EPL];
+    unpack_offsets<BITS>(xo, sp);
+    if constexpr (DIAG) {
+#pragma unroll
+      for (int b = 0; b < EPL / 8; ++b) {
+        float ab[8];
+        lds_block<DK>(ab, vec, aOff + 8 * b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sp[8 * b + i] = (sp[8 * b + i] - F::BIAS) * (in.s * ab[i]);
+      }
+    } else {
+      const float m = in.s * L.alpha_s;
+      const float mb = -F::BIAS * m;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sp[e] = fmaf(sp[e], m, mb);
+    }
+
+    // delta correction u = S' . k and the write coefficient w = beta (v - u)
+    float u = 0.f;
+    if constexpr (DELTA) {
+      float p = 0.f;
+#pragma unroll
+      for (int b = 0; b < EPL / 8; ++b) {
+        float kb[8];
+        lds_block<DK>(kb, vec, kOff + 8 * b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p = fmaf(sp[8 * b + i], kb[i], p);
+      }
+      u = row_sum<LPR>(p);
+    }
+    const float w = L.beta * (in.v - u);
+
+    uint32_t X[NW];
+    // orientation by sign(w) (directional rounding): folded into the sign of
+    // inv so that every update points up; w = 0 has no direction
+    const uint32_t wsign = fbits(w) & 0x80000000u;
+    const float mu = (w == 0.f) ? 0.f : F::MQ;
+    const uint32_t Wm = static_cast<uint32_t>(static_cast<int32_t>(fbits(w)) >> 31);
+    const uint32_t W1 = Wm & F::ONES;
+    // back from the oriented frame: negate offset codes by sign(w), then by sign(k_c)
+    auto unorient = [&](uint32_t x, int j) -> uint32_t {
+      if constexpr (BDR)
+        return ((((x ^ Wm) + W1) ^ L.Kf[j]) + L.K1[j]) ^ F::OFF;
+      else
+        return x ^ F::OFF;
+    };
+    // round one block of eight: S (and S' for BDR) -> offset codes
+    auto round_block = [&](const float* stb, const float* spb, float inv, int b) {
+      float t[8];
+      if constexpr (BDR) {
+        const float inv_w = __uint_as_float(fbits(inv) ^ wsign);
+        float tu[8];
+        fma_ru8(tu, spb, inv_w, mu);                   // ceil(z') + MQ
+        if constexpr (KZ) {
+          float kb[8];
+          lds_block<DK>(kb, vec, kOff + 8 * b);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) tu[i] = (kb[i] == 0.f) ? 0.f : tu[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float tz = fmaf(stb[i], inv_w, F::MQ);  // round half even of z, + MQ
+          t[i] = __builtin_amdgcn_fmed3f(max_bits(tz, tu[i]), F::MQ - F::QMAX, F::MQ + F::QMAX);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          t[i] = __builtin_amdgcn_fmed3f(fmaf(stb[i], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
+      }
+      uint32_t xb[WPB];
+      pack_block<BITS>(t, xb);
+#pragma unroll
+      for (int i = 0; i < WPB; ++i) X[WPB * b + i] = unorient(xb[i], WPB * b + i);
+    };
+
+    float snew = in.s;
+    float po = 0.f;
+    {
+      // rank-one write and readout o_r = S_t . q (before requantisation)
+      float st[EPL];
+#pragma unroll
+      for (int b = 0; b < EPL / 8; ++b) {
+        float kb[8], qb[8];
+        lds_block<DK>(kb, vec, kOff + 8 * b);
+        lds_block<DK>(qb, vec, qOff + 8 * b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          st[8 * b + i] = fmaf(w, kb[i], sp[8 * b + i]);
+          po = fmaf(st[8 * b + i], qb[i], po);
+        }
+      }
+      const float o = row_sum<LPR>(po);
+      if (live && L.lc == 0) a.o[row] = o;
+      float amax = 0.f;
+      if constexpr (POLICY == POL_YOKED) {
+        // advance the fp32 reference row with the same update (natural frame)
+        const int krOff = BDR ? knOff : kOff, qrOff = BDR ? qnOff : qOff;
+#pragma unroll
+        for (int b = 0; b < EPL / 8; ++b) {
+          float ab[8];
+          if constexpr (DIAG) lds_block<DK>(ab, vec, aOff + 8 * b);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) R[8 * b + i] = R[8 * b + i] * (DIAG ? ab[i] : L.alpha_s);
+        }
+        float ur = 0.f;
+        if constexpr (DELTA) {
+          float p = 0.f;
+#pragma unroll
+          for (int b = 0; b < EPL / 8; ++b) {
+            float kb[8];
+            lds_block<DK>(kb, vec, krOff + 8 * b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p = fmaf(R[8 * b + i], kb[i], p);
+          }
+          ur = row_sum<LPR>(p);
+        }
+        const float wr = L.beta * (in.v - ur);
+        float pr = 0.f;
+#pragma unroll
+        for (int b = 0; b < EPL / 8; ++b) {
+          float kb[8], qb[8];
+          lds_block<DK>(kb, vec, krOff + 8 * b);
+          lds_block<DK>(qb, vec, qrOff + 8 * b);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int e = 8 * b + i;
+            R[e] = fmaf(wr, kb[i], R[e]);
+            pr = fmaf(R[e], qb[i], pr);
+            amax = fmaxf(amax, fabsf(R[e]));
+          }
+        }
+        const float oref = row_sum<LPR>(pr);
+        if (live) {
+          store_f32(rp, R);
+          if (L.lc == 0 && a.o_ref) a.o_ref[row] = oref;
+        }
+      } else if constexpr (POLICY == POL_DYNAMIC) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(st[e]));
+      }
+      if constexpr (POLICY != POL_PERSISTENT) snew = group_max(amax, L.gl) / F::QMAX;
+      const float inv = (snew == 0.f) ? 0.f : 1.0f / snew;
+#pragma unroll
+      for (int b = 0; b < EPL / 8; ++b) round_block(&st[8 * b], &sp[8 * b], inv, b);
+    }
+
+    if (live) {
+      uint8_t* p = a.codes + row * ROWB + L.lc * (EPL * BITS / 8);
+#pragma unroll
+      for (int c = 0; c < NW / 4; ++c)
+        reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]);
+      if constexpr (POLICY != POL_PERSISTENT) {
+        if ((L.lc % L.gl) == 0) a.scales[row * a.ng + L.gi] = snew;
+      }
+    }
+  }
+}
+
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSQ_STEP_WAVES_PER_EU)))
+void step_kernel(StepArgs a) {
+  using F = Fmt<BITS>;
+  constexpr int NW = F::NW;
+  constexpr int LPR = DK / EPL;
   constexpr bool BDR = ROUND == RND_BDR;
   static_assert(LPR >= 1 && LPR <= 16, "row must fit a 16-lane DPP row");
 
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wave >= a.total_waves) return;     // whole waves only
-  const int h = wave / a.waves_per_head;
-  const int slice = wave - h * a.waves_per_head;
-  const int lr = lane / LPR;
-  const int lc = lane % LPR;
-  const int col0 = lc * EPL;
-  const int gl = a.group / EPL;          // lanes per group (>= 1)
-  const int gi = col0 / a.group;         // this lane's group
+  Lane<BITS, POLICY, ROUND, DIAG> L;
+  L.h = wave / a.waves_per_head;
+  L.slice = wave - L.h * a.waves_per_head;
+  L.lr = lane / LPR;
+  L.lc = lane % LPR;
+  L.col0 = L.lc * EPL;
+  L.gl = a.group / EPL;                  // lanes per group (>= 1)
+  L.gi = L.col0 / a.group;               // this lane's group
 
-  // per-head vectors for this lane's columns
+  // per-head vectors for this lane's columns (staged in LDS below)
+  __shared__ float4 vec4[4 * kVecs * DK / 4];
+  float* vec = reinterpret_cast<float*>(vec4);
+  L.vbase = (threadIdx.x >> 6) * kVecs * DK;
   float kk[EPL], qq[EPL];
-  load_f32(kk, a.k + (size_t)h * DK + col0);
-  load_f32(qq, a.q + (size_t)h * DK + col0);
-  float aa[DIAG ? EPL : 4];
-  if constexpr (DIAG) load_f32(aa, a.alpha + (size_t)h * DK + col0);
-  const float alpha_s = DIAG ? 1.f : a.alpha[h];
-  const float beta = a.beta[h];
+  load_f32(kk, a.k + (size_t)L.h * DK + L.col0);
+  load_f32(qq, a.q + (size_t)L.h * DK + L.col0);
+  L.alpha_s = DIAG ? 1.f : a.alpha[L.h];
+  L.beta = a.beta[L.h];
+  const bool writer = L.lr == 0;         // one lane per column chunk fills LDS
+  if constexpr (DIAG) {
+    float aa[EPL];
+    load_f32(aa, a.alpha + (size_t)L.h * DK + L.col0);
+    if (writer) store_lds(vec + L.vbase + 2 * DK + L.col0, aa);
+  }
 
-  // Oriented frame for directional rounding: per column rho_c = sign(k_c)
-  // (the sign bit, so -0 counts as negative).  Kf marks, nibble- or byte-wise,
-  // the columns whose codes are negated.  A zero k_c has no update direction:
-  // such a wave patches those elements out of the round-up candidate.
-  uint32_t Kx[BDR ? NW : 1], K1[BDR ? NW : 1], Kf[BDR ? NW : 1];
-  float qn[(BDR && POLICY == POL_YOKED) ? EPL : 4];
-  bool kzero_wave = false;
+  bool kzero = false;
   if constexpr (BDR) {
-    bool kzero = false;
+    // Oriented frame: per column rho_c = sign(k_c) (the sign bit, so -0 counts
+    // as negative).  Kf marks, nibble- or byte-wise, the negated columns.
 #pragma unroll
     for (int e = 0; e < EPL; ++e) kzero |= (kk[e] == 0.f);
-    kzero_wave = __any(kzero);
     // v_perm selector 9 (11) replicates the sign bit of the second (first) operand
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
@@ -293,165 +559,39 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
                             __builtin_amdgcn_perm(fbits(kq[7]), fbits(kq[5]), 0x0B090C0Cu);
         m = (ev & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
       }
-      Kf[j] = m;
-      Kx[j] = m ^ F::OFF;
-      K1[j] = m & F::ONES;
+      L.Kf[j] = m;
+      L.Kx[j] = m ^ F::OFF;
+      L.K1[j] = m & F::ONES;
+    }
+    if constexpr (POLICY == POL_YOKED) {
+      if (writer) {
+        store_lds(vec + L.vbase + 3 * DK + L.col0, kk);
+        store_lds(vec + L.vbase + 4 * DK + L.col0, qq);
+      }
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      if constexpr (POLICY == POL_YOKED) qn[e] = qq[e];
-      qq[e] = __uint_as_float(fbits(qq[e]) ^ (fbits(kk[e]) & 0x80000000u));   // q oriented
+      qq[e] = __uint_as_float(fbits(qq[e]) ^ (fbits(kk[e]) & 0x80000000u));
+      kk[e] = fabsf(kk[e]);
     }
   }
+  if (writer) {
+    store_lds(vec + L.vbase + 0 * DK + L.col0, kk);
+    store_lds(vec + L.vbase + 1 * DK + L.col0, qq);
+  }
+  // LDS accesses of one wave execute in order; the barrier keeps the compiler
+  // from moving reads of the staged vectors above these writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const int it0 = slice * a.nit;
-  auto row_of = [&](int it, bool& live) {
-    const int r = (it0 + it) * RPI + lr;
-    live = r < a.dv;                     // uniform over the lanes of a row
-    return (size_t)h * a.dv + (live ? r : a.dv - 1);
-  };
-
-  RowIn<BITS> nxt;
-  bool live_n;
-  size_t row_n = row_of(0, live_n);
-  load_row<BITS, DK>(nxt, a, row_n, lc, gi);
-
-  for (int it = 0; it < a.nit; ++it) {
-    const RowIn<BITS> in = nxt;
-    const bool live = live_n;
-    const size_t row = row_n;
-    if (it + 1 < a.nit) {
-      row_n = row_of(it + 1, live_n);
-      load_row<BITS, DK>(nxt, a, row_n, lc, gi);
-    }
-    float R[POLICY == POL_YOKED ? EPL : 4];
-    float* rp = a.ref + row * DK + col0;
-    if constexpr (POLICY == POL_YOKED) load_f32(R, rp);
-
-    // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha))
-    uint32_t xo[NW];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      if constexpr (BDR)
-        xo[j] = (in.x[j] ^ Kx[j]) + K1[j];   // offset code, negated where k_c < 0
-      else
-        xo[j] = in.x[j] ^ F::OFF;
-    }
-    float sp[EPL];
-    unpack_offsets<BITS>(xo, sp);
-    if constexpr (DIAG) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float m = in.s * aa[e];
-        sp[e] = (sp[e] - F::BIAS) * m;
-      }
-    } else {
-      const float m = in.s * alpha_s;
-      const float mb = -F::BIAS * m;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sp[e] = fmaf(sp[e], m, mb);
-    }
-
-    // delta correction u = S' . k and the write coefficient w = beta (v - u)
-    float u = 0.f;
-    if constexpr (DELTA) {
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(sp[e], BDR ? fabsf(kk[e]) : kk[e], p);
-      u = row_sum<LPR>(p);
-    }
-    const float w = beta * (in.v - u);
-
-    // rank-one write and readout o_r = S_t . q (before requantisation)
-    float st[EPL];
-    float po = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      st[e] = fmaf(w, BDR ? fabsf(kk[e]) : kk[e], sp[e]);
-      po = fmaf(st[e], qq[e], po);
-    }
-    const float o = row_sum<LPR>(po);
-    if (live && lc == 0) a.o[row] = o;
-
-    // scale policy
-    float snew = in.s;
-    if constexpr (POLICY == POL_YOKED) {
-      // advance the fp32 reference row with the same update (natural frame)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) R[e] = R[e] * (DIAG ? aa[e] : alpha_s);
-      float ur = 0.f;
-      if constexpr (DELTA) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) p = fmaf(R[e], kk[e], p);
-        ur = row_sum<LPR>(p);
-      }
-      const float wr = beta * (in.v - ur);
-      float pr = 0.f, amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        R[e] = fmaf(wr, kk[e], R[e]);
-        pr = fmaf(R[e], BDR ? qn[e] : qq[e], pr);
-        amax = fmaxf(amax, fabsf(R[e]));
-      }
-      const float oref = row_sum<LPR>(pr);
-      if (live) {
-        store_f32(rp, R);
-        if (lc == 0 && a.o_ref) a.o_ref[row] = oref;
-      }
-      snew = group_max(amax, gl) / F::QMAX;
-    } else if constexpr (POLICY == POL_DYNAMIC) {
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(st[e]));
-      snew = group_max(amax, gl) / F::QMAX;
-    }
-    const float inv = (snew == 0.f) ? 0.f : 1.0f / snew;
-
-    // requantise
-    float t[EPL];
-    uint32_t X[NW];
-    if constexpr (BDR) {
-      // orient by sign(w) through the sign of inv: every update now points up
-      const uint32_t wsign = fbits(w) & 0x80000000u;
-      const float inv_w = __uint_as_float(fbits(inv) ^ wsign);
-      const float mu = (w == 0.f) ? 0.f : F::MQ;     // w = 0: no update, no direction
-      float tu[EPL];
-#pragma unroll
-      for (int b = 0; b < EPL / 8; ++b) fma_ru8(&tu[8 * b], &sp[8 * b], inv_w, mu);
-      if (kzero_wave) {   // k_c = 0: no update, so no directional candidate
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) tu[e] = (kk[e] == 0.f) ? 0.f : tu[e];
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float tz = fmaf(st[e], inv_w, F::MQ);   // round half even of z = S*inv
-        t[e] = __builtin_amdgcn_fmed3f(max_bits(tz, tu[e]), F::MQ - F::QMAX, F::MQ + F::QMAX);
-      }
-      pack_offsets<BITS>(t, X);
-      // undo the orientation: negate offset codes by sign(w), then by sign(k_c)
-      const uint32_t Wm = static_cast<uint32_t>(static_cast<int32_t>(fbits(w)) >> 31);
-      const uint32_t W1 = Wm & F::ONES;
-#pragma unroll
-      for (int j = 0; j < NW; ++j) X[j] = ((((X[j] ^ Wm) + W1) ^ Kf[j]) + K1[j]) ^ F::OFF;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        t[e] = __builtin_amdgcn_fmed3f(fmaf(st[e], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
-      pack_offsets<BITS>(t, X);
-#pragma unroll
-      for (int j = 0; j < NW; ++j) X[j] ^= F::OFF;
-    }
-
-    if (live) {
-      uint8_t* p = a.codes + row * ROWB + lc * (EPL * BITS / 8);
-#pragma unroll
-      for (int c = 0; c < NW / 4; ++c)
-        reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]);
-      if constexpr (POLICY != POL_PERSISTENT) {
-        if ((lc % gl) == 0) a.scales[row * a.ng + gi] = snew;
-      }
-    }
+  if constexpr (BDR) {
+    if (__any(kzero))
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, true>(a, L, vec);
+    else
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, false>(a, L, vec);
+  } else {
+    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, false>(a, L, vec);
   }
 }
 
