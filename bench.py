@@ -151,12 +151,12 @@ def main() -> int:
 
     # ---- copy probe for counter calibration (outside the timed region)
     if args.copy_probe_gib > 0:
-        nb = int(args.copy_probe_gib * (1 << 30)) // 4
-        src = torch.ones(nb, device=dev)
+        nbytes = int(args.copy_probe_gib * (1 << 30)) // 256 * 256
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)   # contents irrelevant
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"copy probe: {nb * 4} bytes read and written")
+        log(f"copy probe: one device copy of {nbytes} bytes (read {nbytes}, written {nbytes})")
         del src, dst
 
     # ---- fp32-state comparison at the same shapes (the 'vs FP32 states' context)
