@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
     for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
     amax = group_max(amax, gl);
     const float s = amax / F::QMAX;
-    const float inv = (s == 0.f) ? 0.f : 1.0f / s;
+    const float inv = inv_scale(s);
     float t[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e)

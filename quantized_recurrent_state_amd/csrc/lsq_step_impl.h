@@ -241,10 +241,33 @@ struct RowIn {
   float v;
 };
 
+// Wave-uniform bases of one head's rows (scalar registers); a lane adds a
+// 32-bit offset, so per-row addressing costs a few VALU ops.
+struct HeadPtrs {
+  uint8_t* codes;
+  float* scales;
+  const float* v;
+  float* o;
+  float* o_ref;
+  float* ref;
+};
+
+// Element of a head array at a 32-bit byte offset (a wave-uniform base in
+// scalar registers plus one VGPR: the global_load/store "saddr" form).
+template <typename T>
+__device__ __forceinline__ T& at_bytes(T* base, uint32_t byte_off) {
+  return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ const T& at_bytes(const T* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
 template <int BITS, int DK>
-__device__ __forceinline__ void load_row(RowIn<BITS>& R, const StepArgs& a, size_t row, int lc, int gi) {
+__device__ __forceinline__ void load_row(RowIn<BITS>& R, const HeadPtrs& H, int ng, uint32_t r,
+                                         int lc, int gi) {
   constexpr int ROWB = DK * BITS / 8;
-  const uint8_t* p = a.codes + row * ROWB + lc * (EPL * BITS / 8);
+  const uint8_t* p = H.codes + (r * ROWB + lc * (EPL * BITS / 8));
 #pragma unroll
   for (int c = 0; c < Fmt<BITS>::NW / 4; ++c) {
     const uint4 w = reinterpret_cast<const uint4*>(p)[c];
@@ -253,8 +276,20 @@ __device__ __forceinline__ void load_row(RowIn<BITS>& R, const StepArgs& a, size
     R.x[4 * c + 2] = w.z;
     R.x[4 * c + 3] = w.w;
   }
-  R.s = a.scales[row * a.ng + gi];
-  R.v = a.v[row];
+  R.s = at_bytes(H.scales, (r * ng + gi) * 4u);
+  R.v = at_bytes(H.v, r * 4u);
+}
+
+// fl(1/s): v_rcp_f32 followed by one fma Newton step reproduces the correctly
+// rounded reciprocal for every s in [2^-126, 2^126) on gfx950 (all 2^31
+// positive floats compared with IEEE division; it differs only where s or
+// 1/s is subnormal).  0 and out-of-range scales take the IEEE division.
+__device__ __forceinline__ float inv_scale(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = fmaf(-s, r0, 1.0f);
+  float r = fmaf(e, r0, r0);
+  if (__builtin_expect(!(s >= 0x1p-126f && s < 0x1p126f), 0)) r = (s == 0.f) ? 0.f : 1.0f / s;
+  return r;
 }
 
 #ifndef LSQ_STEP_WAVES_PER_EU
@@ -273,6 +308,7 @@ struct Lane {
   static constexpr int NW = Fmt<BITS>::NW;
   int h, slice, lr, lc, col0, gl, gi;
   int vbase;          // float offset of this wave's vectors in the LDS array
+  HeadPtrs H;         // this head's rows
   float alpha_s, beta;
   uint32_t Kf[BDR ? NW : 1], Kx[BDR ? NW : 1], K1[BDR ? NW : 1];
 };
@@ -305,32 +341,23 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
   constexpr bool BDR = ROUND == RND_BDR;
 
   const int it0 = L.slice * a.nit;
-  auto row_of = [&](int it, bool& live) {
+  const HeadPtrs& H = L.H;
+  auto row_of = [&](int it, bool& live) -> uint32_t {
     const int r = (it0 + it) * RPI + L.lr;
     live = r < a.dv;                     // uniform over the lanes of a row
-    return (size_t)L.h * a.dv + (live ? r : a.dv - 1);
+    return (uint32_t)min(r, a.dv - 1);
   };
 
-  RowIn<BITS> nxt;
-  bool live_n;
-  size_t row_n = row_of(0, live_n);
-  load_row<BITS, DK>(nxt, a, row_n, L.lc, L.gi);
+  // One row, from dequantisation to the packed store.
+  auto process = [&](const RowIn<BITS>& in, const bool live, const uint32_t row) {
 
-  for (int it = 0; it < a.nit; ++it) {
     int base = base0;
     asm volatile("" : "+v"(base));
     const int kOff = base, qOff = base + DK, aOff = base + 2 * DK;
     const int knOff = base + 3 * DK, qnOff = base + 4 * DK;
     (void)qOff; (void)aOff; (void)knOff; (void)qnOff;
-    const RowIn<BITS> in = nxt;
-    const bool live = live_n;
-    const size_t row = row_n;
-    if (it + 1 < a.nit) {
-      row_n = row_of(it + 1, live_n);
-      load_row<BITS, DK>(nxt, a, row_n, L.lc, L.gi);
-    }
     float R[POLICY == POL_YOKED ? EPL : 4];
-    float* rp = a.ref + row * DK + L.col0;
+    float* rp = &at_bytes(H.ref, (row * DK + L.col0) * 4u);
     if constexpr (POLICY == POL_YOKED) load_f32(R, rp);
 
     // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha))
@@ -434,7 +461,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
         }
       }
       const float o = row_sum<LPR>(po);
-      if (live && L.lc == 0) a.o[row] = o;
+      if (live && L.lc == 0) at_bytes(H.o, row * 4u) = o;
       float amax = 0.f;
       if constexpr (POLICY == POL_YOKED) {
         // advance the fp32 reference row with the same update (natural frame)
@@ -476,27 +503,46 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
         const float oref = row_sum<LPR>(pr);
         if (live) {
           store_f32(rp, R);
-          if (L.lc == 0 && a.o_ref) a.o_ref[row] = oref;
+          if (L.lc == 0 && H.o_ref) at_bytes(H.o_ref, row * 4u) = oref;
         }
       } else if constexpr (POLICY == POL_DYNAMIC) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(st[e]));
       }
       if constexpr (POLICY != POL_PERSISTENT) snew = group_max(amax, L.gl) / F::QMAX;
-      const float inv = (snew == 0.f) ? 0.f : 1.0f / snew;
+      const float inv = inv_scale(snew);
 #pragma unroll
       for (int b = 0; b < EPL / 8; ++b) round_block(&st[8 * b], &sp[8 * b], inv, b);
     }
 
     if (live) {
-      uint8_t* p = a.codes + row * ROWB + L.lc * (EPL * BITS / 8);
+      uint8_t* p = H.codes + (row * ROWB + L.lc * (EPL * BITS / 8));
 #pragma unroll
       for (int c = 0; c < NW / 4; ++c)
         reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]);
       if constexpr (POLICY != POL_PERSISTENT) {
-        if ((L.lc % L.gl) == 0) a.scales[row * a.ng + L.gi] = snew;
+        if ((L.lc % L.gl) == 0) at_bytes(H.scales, (row * a.ng + L.gi) * 4u) = snew;
       }
     }
+  };
+
+  // Rows in pairs with two prefetch buffers (no register copies between rows).
+  RowIn<BITS> bufA, bufB;
+  bool liveA, liveB;
+  uint32_t rowA = row_of(0, liveA), rowB = 0;
+  load_row<BITS, DK>(bufA, H, a.ng, rowA, L.lc, L.gi);
+  for (int it = 0; it < a.nit; it += 2) {
+    if (it + 1 < a.nit) {
+      rowB = row_of(it + 1, liveB);
+      load_row<BITS, DK>(bufB, H, a.ng, rowB, L.lc, L.gi);
+    }
+    process(bufA, liveA, rowA);
+    if (it + 1 >= a.nit) break;
+    if (it + 2 < a.nit) {
+      rowA = row_of(it + 2, liveA);
+      load_row<BITS, DK>(bufA, H, a.ng, rowA, L.lc, L.gi);
+    }
+    process(bufB, liveB, rowB);
   }
 }
 
@@ -510,11 +556,20 @@ void step_kernel(StepArgs a) {
   static_assert(LPR >= 1 && LPR <= 16, "row must fit a 16-lane DPP row");
 
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wave >= a.total_waves) return;     // whole waves only
   Lane<BITS, POLICY, ROUND, DIAG> L;
   L.h = wave / a.waves_per_head;
   L.slice = wave - L.h * a.waves_per_head;
+  {
+    const size_t row0 = (size_t)L.h * a.dv;
+    L.H.codes = a.codes + row0 * (DK * BITS / 8);
+    L.H.scales = a.scales + row0 * a.ng;
+    L.H.v = a.v + row0;
+    L.H.o = a.o + row0;
+    L.H.o_ref = a.o_ref ? a.o_ref + row0 : nullptr;
+    L.H.ref = a.ref ? a.ref + row0 * DK : nullptr;
+  }
   L.lr = lane / LPR;
   L.lc = lane % LPR;
   L.col0 = L.lc * EPL;
