@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lsq_internal.h"
 
 namespace lsq {
@@ -310,6 +312,7 @@ struct Lane {
   int vbase;          // float offset of this wave's vectors in the LDS array
   HeadPtrs H;         // this head's rows
   float alpha_s, beta;
+  float alpha_hi;     // max |alpha_c| over the head (the scalar decay's |alpha|)
   uint32_t Kf[BDR ? NW : 1], Kx[BDR ? NW : 1], K1[BDR ? NW : 1];
 };
 
@@ -416,22 +419,29 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
         return x ^ F::OFF;
     };
     // round one block of eight: S (and S' for BDR) -> offset codes
-    auto round_block = [&](const float* stb, const float* spb, float inv, int b) {
+    // IN_RANGE: every ceil(z') of the row lies in [-qmax, qmax], so that
+    // clamp(max(tz, tu)) = med3(tz, tu, MQ + qmax), one instruction.
+    auto round_block = [&](auto in_range, const float* stb, const float* spb, float inv, int b) {
+      constexpr bool IN_RANGE = decltype(in_range)::value;
       float t[8];
       if constexpr (BDR) {
         const float inv_w = __uint_as_float(fbits(inv) ^ wsign);
         float tu[8];
         fma_ru8(tu, spb, inv_w, mu);                   // ceil(z') + MQ
         if constexpr (KZ) {
+          // no update direction where k_c = 0: the candidate is the clamp's floor
           float kb[8];
           lds_block<DK>(kb, vec, kOff + 8 * b);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) tu[i] = (kb[i] == 0.f) ? 0.f : tu[i];
+          for (int i = 0; i < 8; ++i) tu[i] = (kb[i] == 0.f) ? F::MQ - F::QMAX : tu[i];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float tz = fmaf(stb[i], inv_w, F::MQ);  // round half even of z, + MQ
-          t[i] = __builtin_amdgcn_fmed3f(max_bits(tz, tu[i]), F::MQ - F::QMAX, F::MQ + F::QMAX);
+          if constexpr (IN_RANGE)
+            t[i] = __builtin_amdgcn_fmed3f(tz, tu[i], F::MQ + F::QMAX);
+          else
+            t[i] = __builtin_amdgcn_fmed3f(max_bits(tz, tu[i]), F::MQ - F::QMAX, F::MQ + F::QMAX);
         }
       } else {
 #pragma unroll
@@ -511,8 +521,25 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
       }
       if constexpr (POLICY != POL_PERSISTENT) snew = group_max(amax, L.gl) / F::QMAX;
       const float inv = inv_scale(snew);
+      // With an unchanged scale, |z'| = |S'| inv <= fl(qmax fl(s |alpha|)) inv;
+      // when that bound is <= qmax on every lane (any decay with |alpha| below
+      // one by a few ulps), the round-up candidate needs no clamp of its own.
+      // w = 0 (mu = 0) leaves tu = ceil(z') below the clamp's floor and tz
+      // within it, so the median is min(tz, MQ + qmax) there as well.
+      bool in_range = false;
+      if constexpr (BDR && POLICY == POL_PERSISTENT) {
+        const float mq = F::QMAX * fabsf(in.s * L.alpha_hi);
+        in_range = __all(fmaf(mq, inv, -F::QMAX) <= 0.f);
+      }
+      if (in_range) {
 #pragma unroll
-      for (int b = 0; b < EPL / 8; ++b) round_block(&st[8 * b], &sp[8 * b], inv, b);
+        for (int b = 0; b < EPL / 8; ++b)
+          round_block(std::true_type{}, &st[8 * b], &sp[8 * b], inv, b);
+      } else {
+#pragma unroll
+        for (int b = 0; b < EPL / 8; ++b)
+          round_block(std::false_type{}, &st[8 * b], &sp[8 * b], inv, b);
+      }
     }
 
     if (live) {
@@ -584,12 +611,17 @@ void step_kernel(StepArgs a) {
   load_f32(kk, a.k + (size_t)L.h * DK + L.col0);
   load_f32(qq, a.q + (size_t)L.h * DK + L.col0);
   L.alpha_s = DIAG ? 1.f : a.alpha[L.h];
+  L.alpha_hi = fabsf(L.alpha_s);
   L.beta = a.beta[L.h];
   const bool writer = L.lr == 0;         // one lane per column chunk fills LDS
   if constexpr (DIAG) {
     float aa[EPL];
     load_f32(aa, a.alpha + (size_t)L.h * DK + L.col0);
     if (writer) store_lds(vec + L.vbase + 2 * DK + L.col0, aa);
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(aa[e]));
+    L.alpha_hi = group_max(am, LPR);
   }
 
   bool kzero = false;
