@@ -235,6 +235,29 @@ __device__ __forceinline__ void pack_block(const float (&t)[8], uint32_t* X) {
   }
 }
 
+// 16-byte accesses of the packed codes.  Every state byte is written once per
+// step and not read again within it, so the stores carry the non-temporal
+// hint (the nt bit), which speeds up a read-then-write stream on gfx950 (3%
+// on the large steps).  Non-temporal loads gain about as much on states far
+// larger than the last-level cache but lose up to 15% on states that fit it
+// (their next step re-reads them from there), so the loads keep the default.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#ifndef LSQ_NT_CODES
+#define LSQ_NT_CODES 2      // bit 0: loads, bit 1: stores
+#endif
+__device__ __forceinline__ u32x4 load_codes16(const uint8_t* p) {
+  if constexpr ((LSQ_NT_CODES & 1) != 0)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store_codes16(uint8_t* p, u32x4 v) {
+  if constexpr ((LSQ_NT_CODES & 2) != 0)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
 // Per-lane row data, loaded one iteration ahead.
 template <int BITS>
 struct RowIn {
@@ -272,7 +295,7 @@ __device__ __forceinline__ void load_row(RowIn<BITS>& R, const HeadPtrs& H, int 
   const uint8_t* p = H.codes + (r * ROWB + lc * (EPL * BITS / 8));
 #pragma unroll
   for (int c = 0; c < Fmt<BITS>::NW / 4; ++c) {
-    const uint4 w = reinterpret_cast<const uint4*>(p)[c];
+    const u32x4 w = load_codes16(p + 16 * c);
     R.x[4 * c + 0] = w.x;
     R.x[4 * c + 1] = w.y;
     R.x[4 * c + 2] = w.z;
@@ -304,16 +327,30 @@ __device__ __forceinline__ float inv_scale(float s) {
 // staged once per wave in LDS (3 KiB per wave at most) and read per row,
 // which keeps them out of the register file: more waves fit on a SIMD.
 constexpr int kVecs = 5;   // k, q, alpha, natural k, natural q
-template <int BITS, int POLICY, int ROUND, int DIAG>
+// Orientation masks of INT8 codes (three times eight words per lane) live in
+// LDS too; INT4's twelve words stay in registers.
+#ifndef LSQ_MASK_LDS_MIN_BITS
+#define LSQ_MASK_LDS_MIN_BITS 8
+#endif
+template <int BITS, int DK, int ROUND>
+struct LdsPlan {
+  static constexpr int NW = Fmt<BITS>::NW;
+  static constexpr int LPR = DK / EPL;
+  static constexpr bool MASKS = ROUND == RND_BDR && BITS >= LSQ_MASK_LDS_MIN_BITS;
+  static constexpr int MASK_WORDS = MASKS ? 3 * NW * LPR : 0;   // Kf, Kx, K1 per column chunk
+  static constexpr int WAVE_FLOATS = kVecs * DK + MASK_WORDS;
+};
+template <int BITS, int DK, int POLICY, int ROUND, int DIAG>
 struct Lane {
   static constexpr bool BDR = ROUND == RND_BDR;
   static constexpr int NW = Fmt<BITS>::NW;
+  static constexpr bool REG_MASKS = BDR && !LdsPlan<BITS, DK, ROUND>::MASKS;
   int h, slice, lr, lc, col0, gl, gi;
   int vbase;          // float offset of this wave's vectors in the LDS array
   HeadPtrs H;         // this head's rows
   float alpha_s, beta;
   float alpha_hi;     // max |alpha_c| over the head (the scalar decay's |alpha|)
-  uint32_t Kf[BDR ? NW : 1], Kx[BDR ? NW : 1], K1[BDR ? NW : 1];
+  uint32_t Kf[REG_MASKS ? NW : 1], Kx[REG_MASKS ? NW : 1], K1[REG_MASKS ? NW : 1];
 };
 
 // Eight consecutive floats of an LDS vector, read with two 16-byte loads.
@@ -327,14 +364,25 @@ __device__ __forceinline__ void lds_block(float (&d)[8], const float* lds, int o
   d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
   d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
 }
+template <int N>
+__device__ __forceinline__ void lds_words(uint32_t (&d)[N], const float* lds, int off) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const uint4 t = *reinterpret_cast<const uint4*>(lds + off + 4 * i);
+    d[4 * i] = t.x; d[4 * i + 1] = t.y; d[4 * i + 2] = t.z; d[4 * i + 3] = t.w;
+  }
+}
 
 // The row loop of one wave.  KZ: the head's key has a zero component (no
 // update direction there), so those elements drop their round-up candidate.
 template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, bool KZ>
-__device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, ROUND, DIAG>& L,
+__device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DIAG>& L,
                                          const float* vec) {
   // vec + L.vbase + v*DK + L.col0: this lane's 32 columns of vector v
   const int base0 = L.vbase + L.col0;
+  using P = LdsPlan<BITS, DK, ROUND>;
+  // vec + mbase0 + m*LPR*NW: this lane's words of mask m (Kf, Kx, K1)
+  const int mbase0 = L.vbase + kVecs * DK + L.lc * P::NW;
   using F = Fmt<BITS>;
   constexpr int NW = F::NW;
   constexpr int LPR = DK / EPL;          // lanes per row
@@ -356,6 +404,26 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
 
     int base = base0;
     asm volatile("" : "+v"(base));
+    int mbase = mbase0;
+    if constexpr (P::MASKS) asm volatile("" : "+v"(mbase));
+    // words j0 .. j0+N-1 of orientation mask m (0: Kf, 1: Kx, 2: K1)
+    auto mask = [&](int m, int j0, auto& d) {
+      constexpr int N = sizeof(d) / sizeof(d[0]);
+      if constexpr (P::MASKS) {
+        if constexpr (N % 4 == 0) {
+          lds_words<N>(d, vec, mbase + m * LPR * NW + j0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < N; ++j)
+            d[j] = reinterpret_cast<const uint32_t*>(vec)[mbase + m * LPR * NW + j0 + j];
+        }
+      } else if constexpr (BDR) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+          d[j] = m == 0 ? L.Kf[j0 + j] : (m == 1 ? L.Kx[j0 + j] : L.K1[j0 + j]);
+      }
+    };
+    (void)mask;
     const int kOff = base, qOff = base + DK, aOff = base + 2 * DK;
     const int knOff = base + 3 * DK, qnOff = base + 4 * DK;
     (void)qOff; (void)aOff; (void)knOff; (void)qnOff;
@@ -365,12 +433,15 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
 
     // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha))
     uint32_t xo[NW];
+    if constexpr (BDR) {
+      uint32_t kx[NW], k1[NW];
+      mask(1, 0, kx);
+      mask(2, 0, k1);
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      if constexpr (BDR)
-        xo[j] = (in.x[j] ^ L.Kx[j]) + L.K1[j];   // offset code, negated where k_c < 0
-      else
-        xo[j] = in.x[j] ^ F::OFF;
+      for (int j = 0; j < NW; ++j) xo[j] = (in.x[j] ^ kx[j]) + k1[j];   // negated where k_c < 0
+    } else {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) xo[j] = in.x[j] ^ F::OFF;
     }
     float sp[EPL];
     unpack_offsets<BITS>(xo, sp);
@@ -412,9 +483,9 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
     const uint32_t Wm = static_cast<uint32_t>(static_cast<int32_t>(fbits(w)) >> 31);
     const uint32_t W1 = Wm & F::ONES;
     // back from the oriented frame: negate offset codes by sign(w), then by sign(k_c)
-    auto unorient = [&](uint32_t x, int j) -> uint32_t {
+    auto unorient = [&](uint32_t x, uint32_t kf, uint32_t k1) -> uint32_t {
       if constexpr (BDR)
-        return ((((x ^ Wm) + W1) ^ L.Kf[j]) + L.K1[j]) ^ F::OFF;
+        return ((((x ^ Wm) + W1) ^ kf) + k1) ^ F::OFF;
       else
         return x ^ F::OFF;
     };
@@ -448,10 +519,14 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
         for (int i = 0; i < 8; ++i)
           t[i] = __builtin_amdgcn_fmed3f(fmaf(stb[i], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
       }
-      uint32_t xb[WPB];
+      uint32_t xb[WPB], kf[WPB], k1[WPB];
       pack_block<BITS>(t, xb);
+      if constexpr (BDR) {
+        mask(0, WPB * b, kf);
+        mask(2, WPB * b, k1);
+      }
 #pragma unroll
-      for (int i = 0; i < WPB; ++i) X[WPB * b + i] = unorient(xb[i], WPB * b + i);
+      for (int i = 0; i < WPB; ++i) X[WPB * b + i] = unorient(xb[i], kf[i], k1[i]);
     };
 
     float snew = in.s;
@@ -546,7 +621,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, POLICY, R
       uint8_t* p = H.codes + (row * ROWB + L.lc * (EPL * BITS / 8));
 #pragma unroll
       for (int c = 0; c < NW / 4; ++c)
-        reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]);
+        store_codes16(p + 16 * c, u32x4{X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]});
       if constexpr (POLICY != POL_PERSISTENT) {
         if ((L.lc % L.gl) == 0) at_bytes(H.scales, (row * a.ng + L.gi) * 4u) = snew;
       }
@@ -585,7 +660,8 @@ void step_kernel(StepArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wave >= a.total_waves) return;     // whole waves only
-  Lane<BITS, POLICY, ROUND, DIAG> L;
+  Lane<BITS, DK, POLICY, ROUND, DIAG> L;
+  using P = LdsPlan<BITS, DK, ROUND>;
   L.h = wave / a.waves_per_head;
   L.slice = wave - L.h * a.waves_per_head;
   {
@@ -604,9 +680,9 @@ void step_kernel(StepArgs a) {
   L.gi = L.col0 / a.group;               // this lane's group
 
   // per-head vectors for this lane's columns (staged in LDS below)
-  __shared__ float4 vec4[4 * kVecs * DK / 4];
+  __shared__ float4 vec4[4 * P::WAVE_FLOATS / 4];
   float* vec = reinterpret_cast<float*>(vec4);
-  L.vbase = (threadIdx.x >> 6) * kVecs * DK;
+  L.vbase = (threadIdx.x >> 6) * P::WAVE_FLOATS;
   float kk[EPL], qq[EPL];
   load_f32(kk, a.k + (size_t)L.h * DK + L.col0);
   load_f32(qq, a.q + (size_t)L.h * DK + L.col0);
@@ -646,9 +722,18 @@ void step_kernel(StepArgs a) {
                             __builtin_amdgcn_perm(fbits(kq[7]), fbits(kq[5]), 0x0B090C0Cu);
         m = (ev & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
       }
-      L.Kf[j] = m;
-      L.Kx[j] = m ^ F::OFF;
-      L.K1[j] = m & F::ONES;
+      if constexpr (P::MASKS) {
+        if (writer) {
+          float* mp = vec + L.vbase + kVecs * DK + L.lc * NW;
+          reinterpret_cast<uint32_t*>(mp)[j] = m;
+          reinterpret_cast<uint32_t*>(mp + LPR * NW)[j] = m ^ F::OFF;
+          reinterpret_cast<uint32_t*>(mp + 2 * LPR * NW)[j] = m & F::ONES;
+        }
+      } else {
+        L.Kf[j] = m;
+        L.Kx[j] = m ^ F::OFF;
+        L.K1[j] = m & F::ONES;
+      }
     }
     if constexpr (POLICY == POL_YOKED) {
       if (writer) {
