@@ -8,12 +8,12 @@
 // One wavefront owns a slice of rows of one (batch, head).  Each lane owns 32
 // consecutive elements of a row (16 bytes of INT4 or 32 bytes of INT8 codes);
 // Dk/32 lanes cover a row, so a wave covers 64/(Dk/32) rows per iteration and
-// its loads of codes are consecutive in memory.  The lane keeps k and q (and a
-// diagonal decay) for its 32 columns in registers for every row it visits.
-// The two row dot products and the group absmax are reduced across the lanes
-// of a row with DPP butterflies; no LDS, no atomics, no inter-wave traffic.
-// Every step re-reads and re-writes the whole packed state from HBM; the next
-// row's codes, scale and v are loaded while the current row is computed.
+// its loads of codes are consecutive in memory.  The head's vectors (k, q, a
+// diagonal decay) are staged once per wave in LDS and read per row.  The two
+// row dot products and the group absmax are reduced across the lanes of a row
+// with DPP butterflies; no atomics, no inter-wave traffic.  Every step
+// re-reads and re-writes the whole packed state from HBM; the next row's
+// codes, scale and v are loaded while the current row is computed.
 //
 // Instruction budget.  The step is bound by vector-ALU issue, not by the
 // matrix cores (it is a batch of matrix-vector updates), so every element
@@ -34,7 +34,9 @@
 // one grid step toward its update" equals clamp(max(RNE(z), ceil(z'))) with
 // z = S*inv and z' = S'*inv in that frame, i.e. one extra fma rounded toward
 // +infinity (MODE register switched around a block of fmas) and one max per
-// element.  The packed result is turned back by the same xor-add.
+// element (none when the round-up candidate is known to lie in the code
+// range: then one med3 does both).  The packed result is turned back by the
+// same xor-add.
 #pragma once
 
 #include <hip/hip_runtime.h>
