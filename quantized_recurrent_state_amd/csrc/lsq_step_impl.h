@@ -197,6 +197,61 @@ __device__ __forceinline__ void unpack_offsets(const uint32_t (&xo)[Fmt<BITS>::N
   }
 }
 
+// a * b + c with a the low (HI = false) or high half of h taken as binary16,
+// b and c binary32, one rounding to binary32 (v_fma_mix_f32).  An offset code
+// u placed in the low bits of a half is the binary16 subnormal u * 2^-24,
+// converted exactly (binary16 subnormals are kept by the kernel's float mode).
+template <bool HI>
+__device__ __forceinline__ float fma_mix(uint32_t h, float b, float c) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(b), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(b), "v"(c));
+  return d;
+}
+
+// Offset-binary code words -> S' = fl(C * m) = fl(u * m - bias * m), without
+// a separate int -> float conversion: two codes at a time are masked into the
+// low bits of the two halves of a word (binary16 subnormals u * 2^-24, or
+// 16u * 2^-24 for INT4 high nibbles) and v_fma_mix_f32 multiplies them by
+// m * 2^24 (resp. m * 2^20), both exact scalings of m.
+template <int BITS>
+__device__ __forceinline__ void dequant_mix(const uint32_t (&xo)[Fmt<BITS>::NW], float m, float mb,
+                                            float (&f)[EPL]) {
+  const float m24 = m * 0x1p24f;
+  if constexpr (BITS == 4) {
+    const float m20 = m * 0x1p20f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = xo[j];
+      const uint32_t a = x & 0x000F000Fu;          // columns 8j, 8j+4
+      const uint32_t b = x & 0x00F000F0u;          // columns 8j+1, 8j+5 (times 16)
+      const uint32_t c = (x >> 8) & 0x000F000Fu;   // columns 8j+2, 8j+6
+      const uint32_t d = (x >> 8) & 0x00F000F0u;   // columns 8j+3, 8j+7 (times 16)
+      f[8 * j + 0] = fma_mix<false>(a, m24, mb);
+      f[8 * j + 4] = fma_mix<true>(a, m24, mb);
+      f[8 * j + 1] = fma_mix<false>(b, m20, mb);
+      f[8 * j + 5] = fma_mix<true>(b, m20, mb);
+      f[8 * j + 2] = fma_mix<false>(c, m24, mb);
+      f[8 * j + 6] = fma_mix<true>(c, m24, mb);
+      f[8 * j + 3] = fma_mix<false>(d, m20, mb);
+      f[8 * j + 7] = fma_mix<true>(d, m20, mb);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = xo[j];
+      const uint32_t a = x & 0x00FF00FFu;                         // columns 4j, 4j+2
+      const uint32_t b = __builtin_amdgcn_perm(x, x, 0x0C030C01u);  // columns 4j+1, 4j+3
+      f[4 * j + 0] = fma_mix<false>(a, m24, mb);
+      f[4 * j + 2] = fma_mix<true>(a, m24, mb);
+      f[4 * j + 1] = fma_mix<false>(b, m24, mb);
+      f[4 * j + 3] = fma_mix<true>(b, m24, mb);
+    }
+  }
+}
+
 // Gather the low bytes of four words into one word.
 __device__ __forceinline__ uint32_t gather_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // [a0, b0, 0, 0]
@@ -446,8 +501,8 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       for (int j = 0; j < NW; ++j) xo[j] = in.x[j] ^ F::OFF;
     }
     float sp[EPL];
-    unpack_offsets<BITS>(xo, sp);
     if constexpr (DIAG) {
+      unpack_offsets<BITS>(xo, sp);
 #pragma unroll
       for (int b = 0; b < EPL / 8; ++b) {
         float ab[8];
@@ -457,9 +512,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       }
     } else {
       const float m = in.s * L.alpha_s;
-      const float mb = -F::BIAS * m;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sp[e] = fmaf(sp[e], m, mb);
+      dequant_mix<BITS>(xo, m, -F::BIAS * m, sp);
     }
 
     // delta correction u = S' . k and the write coefficient w = beta (v - u)
