@@ -98,8 +98,11 @@ typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
 /* Shape, format and method flags of one handle.
  *   bits   4, 8 (quantised) or 32 (fp32 state, policy NONE)
  *   group  group size along Dk; must divide dk.  This build supports
- *          power-of-two groups of 32 to Dk elements (one lane owns 32
- *          consecutive elements of a row) and Dk in {64, 128}.
+ *          power-of-two groups of 16 to Dk elements (one lane owns 32
+ *          consecutive elements of a row: one group, part of one, or two
+ *          16-element groups) and Dk in {64, 128}.  INT4 with 16-element
+ *          groups and fp32 scales stores 6 bits per element, 5.33x less
+ *          than an fp32 state.
  *   delta  0: linear write, 1: delta-rule correction
  */
 typedef struct {

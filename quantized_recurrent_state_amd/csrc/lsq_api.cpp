@@ -70,11 +70,11 @@ lsq_status check_config(const lsq_config* c) {
   }
   if (c->dk != 64 && c->dk != 128) return fail(LSQ_ERR_UNSUPPORTED, "dk %d: this build has dk 64 and 128", c->dk);
   if (c->bits != 32) {
-    constexpr int epl = 32;   // elements one lane owns
-    if (c->group < epl || (c->group & (c->group - 1)) != 0)
+    constexpr int min_group = 16;   // a lane owns 32 elements: one group, or two of 16
+    if (c->group < min_group || (c->group & (c->group - 1)) != 0)
       return fail(LSQ_ERR_UNSUPPORTED,
                   "group %d: this build needs a power-of-two group of at least %d elements",
-                  c->group, epl);
+                  c->group, min_group);
   }
   const lsq::Geometry g = lsq::geometry(c->bits, c->dk);
   const int64_t iters = (c->dv + g.rows_per_iter - 1) / g.rows_per_iter;

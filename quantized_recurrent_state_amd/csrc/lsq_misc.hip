@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void step_f32_kernel(StepArgs a) {
 }
 
 // Quantise an fp32 state: absmax group scale, round-half-even codes, clamp.
-// Same lane layout as the step kernels (32 elements per lane).
-template <int BITS, int DK>
+// Same lane layout as the step kernels (32 elements per lane); GPL = 2 for
+// 16-element groups (two groups inside a lane).
+template <int BITS, int DK, int GPL>
 __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
   using F = Fmt<BITS>;
   constexpr int LPR = DK / EPL, RPI = 64 / LPR, ROWB = DK * BITS / 8;
@@ -107,16 +108,21 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
     const size_t row = (size_t)h * a.dv + (live ? r : a.dv - 1);
     float x[EPL];
     load_f32(x, a.S + row * DK + col0);
-    float amax = 0.f;
+    float amax[GPL] = {};
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = group_max(amax, gl);
-    const float s = amax / F::QMAX;
-    const float inv = inv_scale(s);
+    for (int e = 0; e < EPL; ++e)
+      amax[GPL == 2 ? e / 16 : 0] = fmaxf(amax[GPL == 2 ? e / 16 : 0], fabsf(x[e]));
+    float s[GPL], inv[GPL];
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      s[g] = (GPL == 2 ? amax[g] : group_max(amax[g], gl)) / F::QMAX;
+      inv[g] = inv_scale(s[g]);
+    }
     float t[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
-      t[e] = __builtin_amdgcn_fmed3f(fmaf(x[e], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
+      t[e] = __builtin_amdgcn_fmed3f(fmaf(x[e], inv[GPL == 2 ? e / 16 : 0], F::MQ), F::MQ - F::QMAX,
+                                     F::MQ + F::QMAX);
     uint32_t X[F::NW];
     pack_offsets<BITS>(t, X);
     if (live) {
@@ -125,7 +131,11 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
       for (int c = 0; c < F::NW / 4; ++c)
         reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c] ^ F::OFF, X[4 * c + 1] ^ F::OFF,
                                                     X[4 * c + 2] ^ F::OFF, X[4 * c + 3] ^ F::OFF);
-      if ((lc % gl) == 0) a.scales[row * a.ng + gi] = s;
+      if constexpr (GPL == 2) {
+        *reinterpret_cast<float2*>(a.scales + row * a.ng + gi) = make_float2(s[0], s[1]);
+      } else {
+        if ((lc % gl) == 0) a.scales[row * a.ng + gi] = s[0];
+      }
       if (a.ref) store_f32(a.ref + row * DK + col0, x);
     }
   }
@@ -157,7 +167,10 @@ hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s)
   const dim3 grid((a.total_waves + 3) / 4), block(256);
 #define LSQ_CAL(B, DK)                                                                  \
   if (bits == B && dk == DK) {                                                          \
-    hipLaunchKernelGGL((dev::calibrate_kernel<B, DK>), grid, block, 0, s, a);           \
+    if (a.group < dev::EPL)                                                             \
+      hipLaunchKernelGGL((dev::calibrate_kernel<B, DK, 2>), grid, block, 0, s, a);      \
+    else                                                                                \
+      hipLaunchKernelGGL((dev::calibrate_kernel<B, DK, 1>), grid, block, 0, s, a);      \
     return hipGetLastError();                                                           \
   }
   LSQ_CAL(4, 128) LSQ_CAL(4, 64) LSQ_CAL(8, 128) LSQ_CAL(8, 64)

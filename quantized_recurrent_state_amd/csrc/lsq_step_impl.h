@@ -216,14 +216,17 @@ __device__ __forceinline__ float fma_mix(uint32_t h, float b, float c) {
 // low bits of the two halves of a word (binary16 subnormals u * 2^-24, or
 // 16u * 2^-24 for INT4 high nibbles) and v_fma_mix_f32 multiplies them by
 // m * 2^24 (resp. m * 2^20), both exact scalings of m.
-template <int BITS>
-__device__ __forceinline__ void dequant_mix(const uint32_t (&xo)[Fmt<BITS>::NW], float m, float mb,
-                                            float (&f)[EPL]) {
-  const float m24 = m * 0x1p24f;
+// With two groups per lane (GPL = 2, 16-element groups) elements 0-15 take
+// m[0] and elements 16-31 m[1].
+template <int BITS, int GPL>
+__device__ __forceinline__ void dequant_mix(const uint32_t (&xo)[Fmt<BITS>::NW], const float (&mm)[GPL],
+                                            const float (&mbb)[GPL], float (&f)[EPL]) {
+  constexpr int NW = Fmt<BITS>::NW;
   if constexpr (BITS == 4) {
-    const float m20 = m * 0x1p20f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const float m = mm[GPL == 2 ? (2 * j) / NW : 0], mb = mbb[GPL == 2 ? (2 * j) / NW : 0];
+      const float m24 = m * 0x1p24f, m20 = m * 0x1p20f;
       const uint32_t x = xo[j];
       const uint32_t a = x & 0x000F000Fu;          // columns 8j, 8j+4
       const uint32_t b = x & 0x00F000F0u;          // columns 8j+1, 8j+5 (times 16)
@@ -241,6 +244,7 @@ __device__ __forceinline__ void dequant_mix(const uint32_t (&xo)[Fmt<BITS>::NW],
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const float m24 = mm[GPL == 2 ? (2 * j) / NW : 0] * 0x1p24f, mb = mbb[GPL == 2 ? (2 * j) / NW : 0];
       const uint32_t x = xo[j];
       const uint32_t a = x & 0x00FF00FFu;                         // columns 4j, 4j+2
       const uint32_t b = __builtin_amdgcn_perm(x, x, 0x0C030C01u);  // columns 4j+1, 4j+3
@@ -316,10 +320,10 @@ __device__ __forceinline__ void store_codes16(uint8_t* p, u32x4 v) {
 }
 
 // Per-lane row data, loaded one iteration ahead.
-template <int BITS>
+template <int BITS, int GPL>
 struct RowIn {
   uint32_t x[Fmt<BITS>::NW];
-  float s;
+  float s[GPL];       // the lane's group scale(s)
   float v;
 };
 
@@ -345,8 +349,8 @@ __device__ __forceinline__ const T& at_bytes(const T* base, uint32_t byte_off) {
   return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
-template <int BITS, int DK>
-__device__ __forceinline__ void load_row(RowIn<BITS>& R, const HeadPtrs& H, int ng, uint32_t r,
+template <int BITS, int DK, int GPL>
+__device__ __forceinline__ void load_row(RowIn<BITS, GPL>& R, const HeadPtrs& H, int ng, uint32_t r,
                                          int lc, int gi) {
   constexpr int ROWB = DK * BITS / 8;
   const uint8_t* p = H.codes + (r * ROWB + lc * (EPL * BITS / 8));
@@ -358,7 +362,13 @@ __device__ __forceinline__ void load_row(RowIn<BITS>& R, const HeadPtrs& H, int 
     R.x[4 * c + 2] = w.z;
     R.x[4 * c + 3] = w.w;
   }
-  R.s = at_bytes(H.scales, (r * ng + gi) * 4u);
+  if constexpr (GPL == 2) {
+    const float2 s2 = at_bytes(reinterpret_cast<const float2*>(H.scales), (r * ng + gi) * 4u);
+    R.s[0] = s2.x;
+    R.s[1] = s2.y;
+  } else {
+    R.s[0] = at_bytes(H.scales, (r * ng + gi) * 4u);
+  }
   R.v = at_bytes(H.v, r * 4u);
 }
 
@@ -432,7 +442,7 @@ __device__ __forceinline__ void lds_words(uint32_t (&d)[N], const float* lds, in
 
 // The row loop of one wave.  KZ: the head's key has a zero component (no
 // update direction there), so those elements drop their round-up candidate.
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, bool KZ>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, bool KZ>
 __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DIAG>& L,
                                          const float* vec) {
   // vec + L.vbase + v*DK + L.col0: this lane's 32 columns of vector v
@@ -457,7 +467,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
   };
 
   // One row, from dequantisation to the packed store.
-  auto process = [&](const RowIn<BITS>& in, const bool live, const uint32_t row) {
+  auto process = [&](const RowIn<BITS, GPL>& in, const bool live, const uint32_t row) {
 
     int base = base0;
     asm volatile("" : "+v"(base));
@@ -508,11 +518,17 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
         float ab[8];
         lds_block<DK>(ab, vec, aOff + 8 * b);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sp[8 * b + i] = (sp[8 * b + i] - F::BIAS) * (in.s * ab[i]);
+        for (int i = 0; i < 8; ++i)
+          sp[8 * b + i] = (sp[8 * b + i] - F::BIAS) * (in.s[GPL == 2 ? b / 2 : 0] * ab[i]);
       }
     } else {
-      const float m = in.s * L.alpha_s;
-      dequant_mix<BITS>(xo, m, -F::BIAS * m, sp);
+      float m[GPL], mb[GPL];
+#pragma unroll
+      for (int h = 0; h < GPL; ++h) {
+        m[h] = in.s[h] * L.alpha_s;
+        mb[h] = -F::BIAS * m[h];
+      }
+      dequant_mix<BITS, GPL>(xo, m, mb, sp);
     }
 
     // delta correction u = S' . k and the write coefficient w = beta (v - u)
@@ -584,7 +600,9 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       for (int i = 0; i < WPB; ++i) X[WPB * b + i] = unorient(xb[i], kf[i], k1[i]);
     };
 
-    float snew = in.s;
+    float snew[GPL];
+#pragma unroll
+    for (int h = 0; h < GPL; ++h) snew[h] = in.s[h];
     float po = 0.f;
     {
       // rank-one write and readout o_r = S_t . q (before requantisation)
@@ -602,7 +620,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       }
       const float o = row_sum<LPR>(po);
       if (live && L.lc == 0) at_bytes(H.o, row * 4u) = o;
-      float amax = 0.f;
+      float amax[GPL] = {};
       if constexpr (POLICY == POL_YOKED) {
         // advance the fp32 reference row with the same update (natural frame)
         const int krOff = BDR ? knOff : kOff, qrOff = BDR ? qnOff : qOff;
@@ -637,7 +655,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
             const int e = 8 * b + i;
             R[e] = fmaf(wr, kb[i], R[e]);
             pr = fmaf(R[e], qb[i], pr);
-            amax = fmaxf(amax, fabsf(R[e]));
+            amax[GPL == 2 ? e / 16 : 0] = fmaxf(amax[GPL == 2 ? e / 16 : 0], fabsf(R[e]));
           }
         }
         const float oref = row_sum<LPR>(pr);
@@ -647,10 +665,20 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
         }
       } else if constexpr (POLICY == POL_DYNAMIC) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(st[e]));
+        for (int e = 0; e < EPL; ++e)
+          amax[GPL == 2 ? e / 16 : 0] = fmaxf(amax[GPL == 2 ? e / 16 : 0], fabsf(st[e]));
       }
-      if constexpr (POLICY != POL_PERSISTENT) snew = group_max(amax, L.gl) / F::QMAX;
-      const float inv = inv_scale(snew);
+      if constexpr (POLICY != POL_PERSISTENT) {
+        if constexpr (GPL == 2) {
+          snew[0] = amax[0] / F::QMAX;               // groups inside the lane
+          snew[1] = amax[1] / F::QMAX;
+        } else {
+          snew[0] = group_max(amax[0], L.gl) / F::QMAX;
+        }
+      }
+      float inv[GPL];
+#pragma unroll
+      for (int h = 0; h < GPL; ++h) inv[h] = inv_scale(snew[h]);
       // With an unchanged scale, |z'| = |S'| inv <= fl(qmax fl(s |alpha|)) inv;
       // when that bound is <= qmax on every lane (any decay with |alpha| below
       // one by a few ulps), the round-up candidate needs no clamp of its own.
@@ -658,17 +686,22 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       // within it, so the median is min(tz, MQ + qmax) there as well.
       bool in_range = false;
       if constexpr (BDR && POLICY == POL_PERSISTENT) {
-        const float mq = F::QMAX * fabsf(in.s * L.alpha_hi);
-        in_range = __all(fmaf(mq, inv, -F::QMAX) <= 0.f);
+        bool ok = true;
+#pragma unroll
+        for (int h = 0; h < GPL; ++h) {
+          const float mq = F::QMAX * fabsf(in.s[h] * L.alpha_hi);
+          ok = ok && fmaf(mq, inv[h], -F::QMAX) <= 0.f;
+        }
+        in_range = __all(ok);
       }
       if (in_range) {
 #pragma unroll
         for (int b = 0; b < EPL / 8; ++b)
-          round_block(std::true_type{}, &st[8 * b], &sp[8 * b], inv, b);
+          round_block(std::true_type{}, &st[8 * b], &sp[8 * b], inv[GPL == 2 ? b / 2 : 0], b);
       } else {
 #pragma unroll
         for (int b = 0; b < EPL / 8; ++b)
-          round_block(std::false_type{}, &st[8 * b], &sp[8 * b], inv, b);
+          round_block(std::false_type{}, &st[8 * b], &sp[8 * b], inv[GPL == 2 ? b / 2 : 0], b);
       }
     }
 
@@ -678,32 +711,36 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       for (int c = 0; c < NW / 4; ++c)
         store_codes16(p + 16 * c, u32x4{X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]});
       if constexpr (POLICY != POL_PERSISTENT) {
-        if ((L.lc % L.gl) == 0) at_bytes(H.scales, (row * a.ng + L.gi) * 4u) = snew;
+        if constexpr (GPL == 2)
+          at_bytes(reinterpret_cast<float2*>(H.scales), (row * a.ng + L.gi) * 4u) =
+              make_float2(snew[0], snew[1]);
+        else if ((L.lc % L.gl) == 0)
+          at_bytes(H.scales, (row * a.ng + L.gi) * 4u) = snew[0];
       }
     }
   };
 
   // Rows in pairs with two prefetch buffers (no register copies between rows).
-  RowIn<BITS> bufA, bufB;
+  RowIn<BITS, GPL> bufA, bufB;
   bool liveA, liveB;
   uint32_t rowA = row_of(0, liveA), rowB = 0;
-  load_row<BITS, DK>(bufA, H, a.ng, rowA, L.lc, L.gi);
+  load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi);
   for (int it = 0; it < a.nit; it += 2) {
     if (it + 1 < a.nit) {
       rowB = row_of(it + 1, liveB);
-      load_row<BITS, DK>(bufB, H, a.ng, rowB, L.lc, L.gi);
+      load_row<BITS, DK, GPL>(bufB, H, a.ng, rowB, L.lc, L.gi);
     }
     process(bufA, liveA, rowA);
     if (it + 1 >= a.nit) break;
     if (it + 2 < a.nit) {
       rowA = row_of(it + 2, liveA);
-      load_row<BITS, DK>(bufA, H, a.ng, rowA, L.lc, L.gi);
+      load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi);
     }
     process(bufB, liveB, rowB);
   }
 }
 
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSQ_STEP_WAVES_PER_EU)))
 void step_kernel(StepArgs a) {
   using F = Fmt<BITS>;
@@ -814,22 +851,27 @@ void step_kernel(StepArgs a) {
 
   if constexpr (BDR) {
     if (__any(kzero))
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, true>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, true>(a, L, vec);
     else
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, false>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, false>(a, L, vec);
   } else {
-    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, false>(a, L, vec);
+    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, false>(a, L, vec);
   }
 }
 
-// Dispatch one (BITS, DK) family over the method flags.
+// Dispatch one (BITS, DK) family over the method flags and the group size
+// (16-element groups: two groups per lane; 32 and more: one).
 template <int BITS, int DK>
 hipError_t launch_family(const StepArgs& a, int policy, int rounding, int delta, int diag,
                          hipStream_t s) {
   const dim3 grid((a.total_waves + 3) / 4), block(256);
+  const int gpl = a.group < EPL ? 2 : 1;   // 16-element groups: two per lane
 #define LSQ_CASE(P, R, D, G)                                                               \
   if (policy == P && rounding == R && delta == D && diag == G) {                           \
-    hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G>), grid, block, 0, s, a);         \
+    if (gpl == 2)                                                                          \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 2>), grid, block, 0, s, a);    \
+    else                                                                                   \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 1>), grid, block, 0, s, a);    \
     return hipGetLastError();                                                              \
   }
 #define LSQ_CASES_PR(P, R) \

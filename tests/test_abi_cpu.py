@@ -43,8 +43,8 @@ BAD = [
     (dict(bits=5), 1), (dict(bits=32, policy=lsq.POLICY_DYNAMIC), 1),
     (dict(policy=lsq.POLICY_NONE), 1), (dict(group=48), 1), (dict(group=0), 1),
     (dict(delta=2), 1), (dict(decay=3), 1), (dict(rounding=7), 1), (dict(batch=-1), 1),
-    (dict(dk=96, group=32), 2), (dict(group=16), 2), (dict(bits=8, group=8), 2),
-    (dict(bits=8, group=16), 2),
+    (dict(dk=96, group=32), 2), (dict(group=8), 2), (dict(bits=8, group=8), 2),
+    (dict(group=24), 1),
     (dict(dk=256, group=32), 2),
 ]
 

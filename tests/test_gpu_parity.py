@@ -80,6 +80,25 @@ def test_step_matches_oracle(bits, dk, pol, rnd, dl, dc):
     assert rep.excused <= max(2, rep.codes // 20000), str(rep)
 
 
+G16 = [(bits, dk, pol, rnd, dc)
+       for bits in (4, 8)
+       for dk in (128, 64)
+       for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT, lsq.POLICY_YOKED)
+       for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+       for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,rnd,dc", G16)
+def test_group16_matches_oracle(bits, dk, pol, rnd, dc):
+    """16-element groups: two groups inside each lane's 32 elements."""
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=44, bits=bits, group=16,
+                        policy=pol, rounding=rnd, delta=1, decay=dc)
+    rep = _run_teacher_forced(cfg, steps=5, recipe="gla" if dc == lsq.DECAY_DIAG else "gdn")
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
 @pytest.mark.parametrize("bits,group", [(4, 64), (4, 128), (8, 32), (8, 128)])
 def test_other_group_sizes(bits, group):
     for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT):
