@@ -30,7 +30,7 @@ _HDR = os.path.join(_HERE, "lsq_oracle.h")
 _LIB = os.path.join(_HERE, "liblsq_oracle.so")
 
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
-ROUND_RNE, ROUND_BDR = 0, 1
+ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
 DECAY_SCALAR, DECAY_DIAG = 0, 1
 
 GCC_FLAGS = ["-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
@@ -52,7 +52,7 @@ def build(force: bool = False) -> str:
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "heads", "dk", "dv", "bits", "group", "policy", "rounding", "delta",
-                 "decay")]
+                 "decay")] + [("step", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
@@ -100,6 +100,7 @@ class OracleConfig:
     rounding: int = ROUND_RNE
     delta: int = 0
     decay: int = DECAY_SCALAR
+    step: int = 0          # sequence position of the (first) step: dithered rounding
 
     @property
     def n(self) -> int:
@@ -178,7 +179,8 @@ def step(cfg: OracleConfig, st: OracleState, q, k, v, alpha, beta, stats: dict |
 
     Returns (o, o_ref); o_ref is None unless the policy is yoked.  With a
     ``trace`` dict (quantised states only), trace["y"] and trace["yp"] receive
-    the exact pre-rounding values S_t*inv and S'*inv in code units.
+    the exact pre-rounding values S_t*inv and S'*inv in code units (dithered
+    rounding: trace["yp"] holds the dither offset u instead of S'*inv).
     """
     _check(cfg)
     q, k, v, alpha, beta = _inputs(cfg, q, k, v, alpha, beta)

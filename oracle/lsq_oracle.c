@@ -24,6 +24,8 @@
  *    the grid of this step (y = S*inv, y' = S'*inv, exact products).  A
  *    reversal is a clamped code c1 with (c1 - y') * sigma_c < 0; it is
  *    replaced by clamp(c1 + sigma_c).
+ *  - dithered rounding: code = clamp(floor(S*inv + u)) with the golden-ratio
+ *    Weyl offset u of the element (see lsq_oracle.h for the sequence).
  */
 #include "lsq_oracle.h"
 
@@ -46,7 +48,9 @@ int lsqo_check_config(const lsqo_config* cfg) {
   if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT &&
       cfg->policy != LSQO_POLICY_YOKED)
     return -1;
-  if (cfg->rounding != LSQO_ROUND_RNE && cfg->rounding != LSQO_ROUND_BDR) return -1;
+  if (cfg->rounding != LSQO_ROUND_RNE && cfg->rounding != LSQO_ROUND_BDR &&
+      cfg->rounding != LSQO_ROUND_DITHER)
+    return -1;
   return 0;
 }
 
@@ -57,6 +61,18 @@ static double round_half_even(double y) {
   if (frac > 0.5) return r + 1.0;
   if (frac < 0.5) return r;
   return (fmod(r, 2.0) == 0.0) ? r : r + 1.0;
+}
+
+/* 2^32 times the golden-ratio conjugate (sqrt(5)-1)/2 = 0.6180339887..., truncated */
+#define LSQO_WEYL_STEP 0x9E3779B9u
+
+/* Weyl dither of element (r, c) of a head at sequence position `step`:
+ * frac(i * 0.618...) in 32-bit fixed point, truncated to 23 bits. */
+static double weyl_dither(int64_t step, int dv, int dk, int r, int c) {
+  const uint32_t i = (uint32_t)((uint64_t)step * (uint64_t)dv * (uint64_t)dk +
+                                (uint64_t)r * (uint64_t)dk + (uint64_t)c);
+  const uint32_t w = i * LSQO_WEYL_STEP; /* mod 2^32 */
+  return (double)(w >> 9) * 0x1p-23;
 }
 
 static double clampd(double x, double lo, double hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -181,7 +197,17 @@ static void step_heads(step_job* J) {
             J->y_out[(h * dv + r) * (int64_t)dk + c] = y;
             J->yp_out[(h * dv + r) * (int64_t)dk + c] = (double)sp[c] * (double)inv;
           }
-          double c0 = round_half_even(y);
+          double c0;
+          if (cfg->rounding == LSQO_ROUND_DITHER) {
+            /* floor(y + u), decided exactly: y - floor(y) and 1 - u are exact
+             * (y has at most 48 significant bits, u 23 bits below the point) */
+            const double u = weyl_dither(cfg->step, dv, dk, r, c);
+            const double fy = floor(y);
+            c0 = fy + ((y - fy >= 1.0 - u) ? 1.0 : 0.0);
+            if (J->yp_out) J->yp_out[(h * dv + r) * (int64_t)dk + c] = u;
+          } else {
+            c0 = round_half_even(y);
+          }
           double c1 = clampd(c0, -qm, qm);
           if (c1 != c0) J->stats.clamped++;
           double c2 = c1;
@@ -247,7 +273,10 @@ static void* run_worker(void* arg) {
   const int64_t n = R->n;
   const int64_t dk = cfg->dk, dv = cfg->dv;
   const int64_t astride = (cfg->decay == LSQO_DECAY_DIAG) ? n * dk : n;
+  lsqo_config ct = *cfg;
+  J.cfg = &ct;
   for (int32_t t = 0; t < R->H; ++t) {
+    ct.step = cfg->step + t;
     J.q = R->job.q + t * n * dk;
     J.k = R->job.k + t * n * dk;
     J.v = R->job.v + t * n * dv;

@@ -26,6 +26,15 @@
  *  - "Preserving Updates in Low-Bit Recurrent State Quantization" (abstract):
  *    Bounded Directional Rounding rounds an element whose rounded value moved
  *    opposite to its update one step toward that update.
+ *  - "Low-Discrepancy Dither for Quantized Recurrent State Caches" (listing
+ *    entry): a deterministic golden-ratio Weyl dither, no random numbers,
+ *    replaces plain rounding of the recurrent state.  The entry fixes nothing
+ *    else; the reading implemented here (LSQO_ROUND_DITHER): the code is
+ *    clamp(floor(S*inv + u)), u the Weyl sequence frac(i * (sqrt(5)-1)/2)
+ *    taken in 32-bit fixed point (w = i * 0x9E3779B9 mod 2^32) and truncated
+ *    to 23 bits (u = (w >> 9) * 2^-23), i = step * Dv * Dk + r * Dk + c the
+ *    element's position in one sequence that runs through the head's state
+ *    row by row, step after step (i taken mod 2^32).
  *
  * State layout used by the oracle (unpacked, host memory, heads = batch*heads):
  *   codes  int8  [heads][Dv][Dk]        signed codes in [-qmax, qmax]
@@ -46,7 +55,7 @@ extern "C" {
 
 /* enumerations (numeric values mirror the public interface by necessity) */
 enum { LSQO_POLICY_NONE = 0, LSQO_POLICY_DYNAMIC = 1, LSQO_POLICY_PERSISTENT = 2, LSQO_POLICY_YOKED = 3 };
-enum { LSQO_ROUND_RNE = 0, LSQO_ROUND_BDR = 1 };
+enum { LSQO_ROUND_RNE = 0, LSQO_ROUND_BDR = 1, LSQO_ROUND_DITHER = 2 };
 enum { LSQO_DECAY_SCALAR = 0, LSQO_DECAY_DIAG = 1 };
 
 typedef struct {
@@ -57,6 +66,7 @@ typedef struct {
   int32_t rounding; /* LSQO_ROUND_* */
   int32_t delta;    /* 0: linear write, 1: delta-rule correction */
   int32_t decay;    /* LSQO_DECAY_* */
+  int64_t step;     /* sequence position of the (first) step: dithered rounding */
 } lsqo_config;
 
 /* counters filled by a step (nullable): element-steps whose code was clamped
