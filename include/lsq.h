@@ -21,7 +21,9 @@
  * and rounded either to nearest-even or by Bounded Directional Rounding
  * ("Preserving Updates in Low-Bit Recurrent State Quantization", abstract): an
  * element whose rounded value moved opposite to its update is rounded one
- * grid step toward the update.
+ * grid step toward the update, or with a deterministic golden-ratio Weyl
+ * dither ("Low-Discrepancy Dither for Quantized Recurrent State Caches",
+ * listing entry; the sequence below is this library's reading of it).
  *
  * Arithmetic contract (every step below is what the kernels compute):
  *   m_c   = fl(s_group(c) * alpha_c)            alpha_c = alpha for scalar decay
@@ -36,6 +38,10 @@
  *   c1    = clamp(round-half-even(S_c * inv exactly), -qmax, qmax)
  *   BDR:    sigma_c = sign(w) sign(k_c); if (c1 - S'_c * inv) * sigma_c < 0
  *           (exact), then c = clamp(c1 + sigma_c), else c = c1
+ *   DITHER: c = clamp(floor(S_c * inv + u_i) exactly, -qmax, qmax) in place of
+ *           c1, u_i = ((i * 0x9E3779B9) mod 2^32 >> 9) * 2^-23 (the Weyl
+ *           sequence frac(i (sqrt(5)-1)/2) in fixed point, 23 bits), i =
+ *           (t Dv Dk + r Dk + c) mod 2^32 with t the handle's step index
  * with qmax = 2^(bits-1) - 1 (7 for INT4, 127 for INT8).
  *
  * Memory: every pointer below is a DEVICE pointer (row-major, 16-byte
@@ -92,7 +98,7 @@ typedef enum {
   LSQ_POLICY_YOKED = 3
 } lsq_policy;
 
-typedef enum { LSQ_ROUND_RNE = 0, LSQ_ROUND_BDR = 1 } lsq_rounding;
+typedef enum { LSQ_ROUND_RNE = 0, LSQ_ROUND_BDR = 1, LSQ_ROUND_DITHER = 2 } lsq_rounding;
 typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
 
 /* Shape, format and method flags of one handle.
@@ -152,6 +158,14 @@ lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream);
 /* Declare that the bound scale buffer already holds frozen scales (resuming a
  * persistent-policy state from a copy of its buffers). */
 lsq_status lsq_state_set_calibrated(lsq_state* st, int32_t calibrated);
+
+/* The handle's step index t: the sequence position the next step uses for
+ * dithered rounding.  It starts at 0 (lsq_state_alloc, lsq_state_zero) and
+ * advances by one per step (lsq_decode_run: by H), whatever the rounding.
+ * A checkpoint restores it with lsq_state_set_step_index (t >= 0, else
+ * INVALID_ARG).  Host-only calls, no device work. */
+lsq_status lsq_state_step_index(const lsq_state* st, int64_t* t);
+lsq_status lsq_state_set_step_index(lsq_state* st, int64_t t);
 
 /* One decode step for all heads (shapes above).  alpha has [heads] or
  * [heads][Dk] entries by the decay flag.  o_ref may be NULL; it is written

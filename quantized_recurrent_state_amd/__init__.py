@@ -15,11 +15,12 @@ from . import _lib
 from ._lib import LsqError
 
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
-ROUND_RNE, ROUND_BDR = 0, 1
+ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
 DECAY_SCALAR, DECAY_DIAG = 0, 1
 
 __all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_alloc",
            "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_set_calibrated",
+           "lsq_state_step_index", "lsq_state_set_step_index",
            "lsq_decode_step", "lsq_decode_run", "lsq_status_string", "lsq_version"]
 
 
@@ -95,6 +96,16 @@ def lsq_state_set_calibrated(handle: int, calibrated: bool = True) -> None:
                "lsq_state_set_calibrated")
 
 
+def lsq_state_step_index(handle: int) -> int:
+    t = ctypes.c_int64(0)
+    _lib.check(_lib.load().lsq_state_step_index(handle, ctypes.byref(t)), "lsq_state_step_index")
+    return int(t.value)
+
+
+def lsq_state_set_step_index(handle: int, t: int) -> None:
+    _lib.check(_lib.load().lsq_state_set_step_index(handle, int(t)), "lsq_state_set_step_index")
+
+
 def lsq_decode_step(handle: int, q, k, v, alpha, beta, o, o_ref=None, stream=None) -> None:
     _lib.check(_lib.load().lsq_decode_step(handle, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                            _ptr(beta), _ptr(o), _ptr(o_ref), _stream_ptr(stream)),
@@ -157,6 +168,15 @@ class LsqState:
     def set_calibrated(self, calibrated=True):
         lsq_state_set_calibrated(self.handle, calibrated)
         return self
+
+    @property
+    def step_index(self) -> int:
+        """Sequence position of the next step (dithered rounding)."""
+        return lsq_state_step_index(self.handle)
+
+    @step_index.setter
+    def step_index(self, t: int) -> None:
+        lsq_state_set_step_index(self.handle, t)
 
     def _out(self, o, lead):
         import torch

@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
         "lsq_state_zero": [P, P],
         "lsq_state_calibrate": [P, P, P],
         "lsq_state_set_calibrated": [P, ctypes.c_int32],
+        "lsq_state_step_index": [P, ctypes.POINTER(ctypes.c_int64)],
+        "lsq_state_set_step_index": [P, ctypes.c_int64],
         "lsq_decode_step": [P, P, P, P, P, P, P, P, P],
         "lsq_decode_run": [P, ctypes.c_int32, P, P, P, P, P, P, P, P],
         "lsq_status_string": [ctypes.c_int],

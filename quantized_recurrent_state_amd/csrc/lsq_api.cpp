@@ -18,6 +18,7 @@ struct lsq_state {
   float* ref;
   float* f32;
   int32_t calibrated;
+  int64_t step;          // sequence position of the next step (dithered rounding)
 };
 
 namespace {
@@ -54,8 +55,9 @@ lsq_status check_config(const lsq_config* c) {
   if (c->delta != 0 && c->delta != 1) return fail(LSQ_ERR_INVALID_ARG, "delta must be 0 or 1");
   if (c->decay != LSQ_DECAY_SCALAR && c->decay != LSQ_DECAY_DIAG)
     return fail(LSQ_ERR_INVALID_ARG, "decay must be SCALAR or DIAG");
-  if (c->rounding != LSQ_ROUND_RNE && c->rounding != LSQ_ROUND_BDR)
-    return fail(LSQ_ERR_INVALID_ARG, "rounding must be RNE or BDR");
+  if (c->rounding != LSQ_ROUND_RNE && c->rounding != LSQ_ROUND_BDR &&
+      c->rounding != LSQ_ROUND_DITHER)
+    return fail(LSQ_ERR_INVALID_ARG, "rounding must be RNE, BDR or DITHER");
   if (c->bits == 32) {
     if (c->policy != LSQ_POLICY_NONE)
       return fail(LSQ_ERR_INVALID_ARG, "an fp32 state (bits 32) takes policy NONE");
@@ -141,6 +143,9 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
   a.group = c.group;
   a.ng = (c.bits == 32) ? 0 : c.dk / c.group;
   choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves);
+  constexpr uint32_t kWeyl = 0x9E3779B9u;   // 2^32 (sqrt(5)-1)/2, truncated
+  a.dither_base = (uint32_t)((uint64_t)st->step * (uint64_t)c.dv * (uint64_t)c.dk) * kWeyl;
+  a.dither_row = (uint32_t)c.dk * kWeyl;
   hipError_t e;
   if (c.bits == 32)
     e = lsq::launch_step_f32(a, c.dk, c.delta, c.decay, stream);
@@ -148,7 +153,9 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
     e = lsq::launch_step_q4(a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   else
     e = lsq::launch_step_q8(a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
-  return hip_status(e, "decode-step launch");
+  lsq_status s = hip_status(e, "decode-step launch");
+  if (s == LSQ_OK) ++st->step;
+  return s;
 }
 
 }  // namespace
@@ -195,6 +202,7 @@ lsq_status lsq_state_alloc(const lsq_config* cfg, const lsq_buffers* bufs, lsq_s
   st->ref = need[2] ? bufs->ref : nullptr;
   st->f32 = need[3] ? bufs->f32 : nullptr;
   st->calibrated = 0;
+  st->step = 0;
   *out = st;
   return ok();
 }
@@ -219,6 +227,7 @@ lsq_status lsq_state_zero(lsq_state* st, void* stream) {
     if (s != LSQ_OK) return s;
   }
   st->calibrated = 0;
+  st->step = 0;
   return ok();
 }
 
@@ -260,13 +269,29 @@ lsq_status lsq_state_set_calibrated(lsq_state* st, int32_t calibrated) {
   return ok();
 }
 
+lsq_status lsq_state_step_index(const lsq_state* st, int64_t* out) {
+  if (!st || !out) return fail(LSQ_ERR_INVALID_ARG, "null argument");
+  *out = st->step;
+  return ok();
+}
+
+lsq_status lsq_state_set_step_index(lsq_state* st, int64_t step) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  if (step < 0) return fail(LSQ_ERR_INVALID_ARG, "negative step index");
+  st->step = step;
+  return ok();
+}
+
 lsq_status lsq_decode_step(lsq_state* st, const float* q, const float* k, const float* v,
                            const float* alpha, const float* beta, float* o, float* o_ref,
                            void* stream) {
   if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
   if (st->cfg.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
     return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");
-  if (n_heads(st->cfg) == 0) return ok();   // nothing to read or write
+  if (n_heads(st->cfg) == 0) {   // nothing to read or write
+    ++st->step;
+    return ok();
+  }
   lsq_status s = check_step_ptrs(st, q, k, v, alpha, beta, o);
   if (s != LSQ_OK) return s;
   return launch_one_step(st, q, k, v, alpha, beta, o, o_ref, static_cast<hipStream_t>(stream));
@@ -279,7 +304,10 @@ lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float*
   if (H < 0) return fail(LSQ_ERR_INVALID_ARG, "negative horizon");
   if (st->cfg.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
     return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");
-  if (H == 0 || n_heads(st->cfg) == 0) return ok();   // nothing to read or write
+  if (H == 0 || n_heads(st->cfg) == 0) {   // nothing to read or write
+    st->step += H;
+    return ok();
+  }
   lsq_status s = check_step_ptrs(st, q, k, v, alpha, beta, o);
   if (s != LSQ_OK) return s;
   const lsq_config& c = st->cfg;
@@ -309,6 +337,6 @@ const char* lsq_status_string(lsq_status s) {
 
 const char* lsq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t lsq_version(void) { return 100; }
+int32_t lsq_version(void) { return 101; }
 
 }  // extern "C"

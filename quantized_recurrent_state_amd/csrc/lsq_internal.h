@@ -27,6 +27,10 @@ struct StepArgs {
   int32_t nit;           // row-iterations per wave
   int32_t waves_per_head;
   int32_t total_waves;
+  // dithered rounding: Weyl state of element (r, c) of every head is
+  // dither_base + r * dither_row + c * 0x9E3779B9 (mod 2^32)
+  uint32_t dither_base;  // (step * dv * dk) * 0x9E3779B9 mod 2^32
+  uint32_t dither_row;   // dk * 0x9E3779B9 mod 2^32
 };
 
 // Arguments of a calibration launch: quantise an fp32 state into codes/scales.

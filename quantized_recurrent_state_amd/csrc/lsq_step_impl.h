@@ -50,7 +50,12 @@ namespace lsq {
 namespace dev {
 
 enum { POL_DYNAMIC = 1, POL_PERSISTENT = 2, POL_YOKED = 3 };
-enum { RND_RNE = 0, RND_BDR = 1 };
+enum { RND_RNE = 0, RND_BDR = 1, RND_DITHER = 2 };
+
+// Golden-ratio Weyl dither: 2^32 (sqrt(5)-1)/2, truncated.  The offset of
+// sequence position i is frac(i * 0.618...) = ((i * kWeyl) mod 2^32) / 2^32,
+// used with 23 bits: the float 1 + u is 0x3F800000 | (w >> 9).
+constexpr uint32_t kWeyl = 0x9E3779B9u;
 
 // 1.5 * 2^23: adding it to |y| < 2^22 with one rounding leaves
 // round-half-even(y) in the low mantissa bits (spacing 1 in [2^23, 2^24)).
@@ -154,6 +159,38 @@ __device__ __forceinline__ void fma_ru8(float* d, const float* a, float b, float
       : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
         "=&v"(d[6]), "=&v"(d[7])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(b), "v"(c));
+}
+
+// d[i] = (a[i] * b + e[i]) + c, both operations rounded toward -infinity:
+// with e = 1 + u and c = MQ - 1 this is MQ + floor(a*b + u) exactly (the
+// first rounding keeps the floor, the second lands on the integer grid).
+__device__ __forceinline__ void fma_add_rd8(float* d, const float* a, float b, const float* e, float c) {
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 2\n\t"
+      "s_nop 1\n\t"
+      "v_fma_f32 %0, %8, %24, %16\n\t"
+      "v_fma_f32 %1, %9, %24, %17\n\t"
+      "v_fma_f32 %2, %10, %24, %18\n\t"
+      "v_fma_f32 %3, %11, %24, %19\n\t"
+      "v_fma_f32 %4, %12, %24, %20\n\t"
+      "v_fma_f32 %5, %13, %24, %21\n\t"
+      "v_fma_f32 %6, %14, %24, %22\n\t"
+      "v_fma_f32 %7, %15, %24, %23\n\t"
+      "v_add_f32 %0, %0, %25\n\t"
+      "v_add_f32 %1, %1, %25\n\t"
+      "v_add_f32 %2, %2, %25\n\t"
+      "v_add_f32 %3, %3, %25\n\t"
+      "v_add_f32 %4, %4, %25\n\t"
+      "v_add_f32 %5, %5, %25\n\t"
+      "v_add_f32 %6, %6, %25\n\t"
+      "v_add_f32 %7, %7, %25\n\t"
+      "s_nop 1\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
+        "=&v"(d[6]), "=&v"(d[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(e[0]), "v"(e[1]), "v"(e[2]), "v"(e[3]), "v"(e[4]), "v"(e[5]), "v"(e[6]), "v"(e[7]),
         "v"(b), "v"(c));
 }
 
@@ -560,6 +597,9 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       else
         return x ^ F::OFF;
     };
+    // Weyl sequence position of this lane's first element of the row
+    const uint32_t dbase = a.dither_base + row * a.dither_row + (uint32_t)L.col0 * kWeyl;
+    (void)dbase;
     // round one block of eight: S (and S' for BDR) -> offset codes
     // IN_RANGE: every ceil(z') of the row lies in [-qmax, qmax], so that
     // clamp(max(tz, tu)) = med3(tz, tu, MQ + qmax), one instruction.
@@ -585,6 +625,15 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
           else
             t[i] = __builtin_amdgcn_fmed3f(max_bits(tz, tu[i]), F::MQ - F::QMAX, F::MQ + F::QMAX);
         }
+      } else if constexpr (ROUND == RND_DITHER) {
+        // floor(z + u) with the Weyl offsets of elements 8b .. 8b+7
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          e[i] = __uint_as_float(0x3F800000u | ((dbase + (uint32_t)(8 * b + i) * kWeyl) >> 9));
+        fma_add_rd8(t, stb, inv, e, F::MQ - 1.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], F::MQ - F::QMAX, F::MQ + F::QMAX);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -876,7 +925,7 @@ hipError_t launch_family(const StepArgs& a, int policy, int rounding, int delta,
   }
 #define LSQ_CASES_PR(P, R) \
   LSQ_CASE(P, R, 0, 0) LSQ_CASE(P, R, 0, 1) LSQ_CASE(P, R, 1, 0) LSQ_CASE(P, R, 1, 1)
-#define LSQ_CASES_P(P) LSQ_CASES_PR(P, RND_RNE) LSQ_CASES_PR(P, RND_BDR)
+#define LSQ_CASES_P(P) LSQ_CASES_PR(P, RND_RNE) LSQ_CASES_PR(P, RND_BDR) LSQ_CASES_PR(P, RND_DITHER)
   LSQ_CASES_P(POL_DYNAMIC)
   LSQ_CASES_P(POL_PERSISTENT)
   LSQ_CASES_P(POL_YOKED)

@@ -10,8 +10,9 @@ Bar (taken from the decode-step contract):
   * codes bit-exact, except a code that differs by exactly 1 where the
     oracle's exact pre-rounding value lies within BAND_REL * qmax code units of
     the decision boundary (the half-integer of round-half-even, or for
-    directional rounding the pre-update value y' against the candidate code);
-    such cases are counted and reported;
+    directional rounding the pre-update value y' against the candidate code,
+    for dithered rounding the integers against y + u); such cases are counted
+    and reported;
   * dynamic and yoked scales within 1e-6 relative, persistent scales exact;
   * outputs o (and o_ref) with ||o_gpu - o_oracle||_inf <= 1e-4 ||o_oracle||_inf
     per head;
@@ -26,7 +27,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 import oracle
-from oracle import OracleConfig, OracleState, POLICY_YOKED, POLICY_PERSISTENT, ROUND_BDR
+from oracle import (OracleConfig, OracleState, POLICY_YOKED, POLICY_PERSISTENT, ROUND_BDR,
+                    ROUND_DITHER)
 
 BAND_REL = 1e-6
 O_TOL = 1e-4
@@ -34,10 +36,12 @@ REF_TOL = 1e-5
 SCALE_TOL = 1e-6
 
 
-def ocfg_of(cfg) -> OracleConfig:
+def ocfg_of(cfg, step: int = 0) -> OracleConfig:
+    """The oracle configuration of a GPU handle's configuration; `step` is the
+    handle's step index before the step (the dither's sequence position)."""
     return OracleConfig(batch=cfg.batch, heads=cfg.heads, dk=cfg.dk, dv=cfg.dv, bits=cfg.bits,
                         group=cfg.group, policy=cfg.policy, rounding=cfg.rounding,
-                        delta=cfg.delta, decay=cfg.decay)
+                        delta=cfg.delta, decay=cfg.decay, step=step)
 
 
 def snapshot(gpu_state, heads=None) -> OracleState:
@@ -100,6 +104,10 @@ def _normwise(got, want):
 
 def boundary_distance(y, yp, codes_oracle, rounding):
     """Distance of the exact values to the decision boundary of each element."""
+    if rounding == ROUND_DITHER:
+        # floor(y + u): the boundaries are the integers (yp holds the dither u)
+        z = y + yp
+        return np.abs(z - np.round(z))
     d = np.abs(y - (np.floor(y) + 0.5))
     d = np.minimum(d, np.abs(y - (np.floor(y) - 0.5)))
     d = np.minimum(d, np.abs(y - (np.floor(y) + 1.5)))

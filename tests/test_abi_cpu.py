@@ -116,3 +116,24 @@ def test_empty_batch_calls_are_noops():
 def test_status_strings():
     for s in range(6):
         assert lsq.lsq_status_string(s).startswith(_lib.STATUS_NAMES[s])
+
+
+def test_step_index_is_host_state():
+    L = _lib.load()
+    cfg = lsq.LsqConfig(1, 2, 128, 16, 4, 32, lsq.POLICY_DYNAMIC, lsq.ROUND_DITHER)
+    st, h = _alloc(cfg)
+    assert st == 0
+    assert lsq.lsq_state_step_index(h) == 0
+    lsq.lsq_state_set_step_index(h, 5)
+    assert lsq.lsq_state_step_index(h) == 5
+    with pytest.raises(lsq.LsqError) as e:
+        lsq.lsq_state_set_step_index(h, -1)
+    assert e.value.status == 1
+    lsq.lsq_state_free(h)
+    # an empty batch still advances the sequence position (no device work)
+    cfg0 = lsq.LsqConfig(0, 4, 128, 128, 4, 32, lsq.POLICY_DYNAMIC, lsq.ROUND_DITHER)
+    st, h = _alloc(cfg0, codes=None, scales=None)
+    assert L.lsq_decode_step(h, None, None, None, None, None, None, None, None) == 0
+    assert L.lsq_decode_run(h, 3, None, None, None, None, None, None, None, None) == 0
+    assert lsq.lsq_state_step_index(h) == 4
+    lsq.lsq_state_free(h)

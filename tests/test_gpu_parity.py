@@ -49,11 +49,14 @@ def _run_teacher_forced(cfg, steps, recipe, warmup=4):
         t0 = warmup
     dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, t0, steps)
     before = snapshot(st)
+    if cfg.rounding == lsq.ROUND_DITHER:
+        st.step_index = 1000 + 37 * cfg.dk     # any position: the sequence is stateless
     for t in range(steps):
+        ocfg_t = ocfg.replace(step=st.step_index)
         out = st.step(dg["q"][t], dg["k"][t], dg["v"][t], dg["alpha"][t], dg["beta"][t])
         o, o_ref = out if cfg.policy == lsq.POLICY_YOKED else (out, None)
         after = snapshot(st)
-        rep.add(compare_step(ocfg, before, _np_step(dn, t), after, o.cpu().numpy(),
+        rep.add(compare_step(ocfg_t, before, _np_step(dn, t), after, o.cpu().numpy(),
                              None if o_ref is None else o_ref.cpu().numpy()))
         before = after
     return rep
@@ -63,7 +66,7 @@ COMBOS = [(bits, dk, pol, rnd, dl, dc)
           for bits in (4, 8)
           for dk in (128, 64)
           for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT, lsq.POLICY_YOKED)
-          for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+          for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR, lsq.ROUND_DITHER)
           for dl in (0, 1)
           for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
 
@@ -84,7 +87,7 @@ G16 = [(bits, dk, pol, rnd, dc)
        for bits in (4, 8)
        for dk in (128, 64)
        for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT, lsq.POLICY_YOKED)
-       for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+       for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR, lsq.ROUND_DITHER)
        for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
 
 
@@ -140,6 +143,31 @@ def test_run_equals_repeated_steps_and_is_deterministic():
     for x, y in ((a, b), (a, c)):
         assert torch.equal(x.codes, y.codes) and torch.equal(x.scales, y.scales)
     assert torch.equal(oa, ob) and torch.equal(oa, oc)
+
+
+def test_dither_step_index_drives_the_sequence():
+    """The step index advances per step and per run; restoring it resumes the
+    same dithered trajectory; the same state at another index differs."""
+    cfg = lsq.LsqConfig(batch=2, heads=4, dk=128, dv=64, bits=4, group=32,
+                        policy=lsq.POLICY_PERSISTENT, rounding=lsq.ROUND_DITHER, delta=1, decay=0)
+    dg, _ = _inputs("gdn", cfg.n, 128, 64, 0, 8)
+    S0 = torch.randn(cfg.n, 64, 128, device=DEV) * 0.1
+    a = lsq.LsqState(cfg, device=DEV).zero().calibrate(S0)
+    b = lsq.LsqState(cfg, device=DEV).zero().calibrate(S0)
+    assert a.step_index == 0
+    oa = a.run(*(dg[x] for x in ("q", "k", "v", "alpha", "beta")))
+    assert a.step_index == 8
+    ob = torch.stack([b.step(*(dg[x][t] for x in ("q", "k", "v", "alpha", "beta"))) for t in range(8)])
+    assert b.step_index == 8
+    assert torch.equal(oa, ob) and torch.equal(a.codes, b.codes)
+    c = lsq.LsqState(cfg, device=DEV).zero().calibrate(S0)
+    c.step_index = 5
+    c.step(*(dg[x][0] for x in ("q", "k", "v", "alpha", "beta")))
+    d = lsq.LsqState(cfg, device=DEV).zero().calibrate(S0)
+    d.step(*(dg[x][0] for x in ("q", "k", "v", "alpha", "beta")))
+    assert not torch.equal(c.codes, d.codes)
+    with pytest.raises(lsq.LsqError, match="INVALID_ARG"):
+        c.step_index = -1
 
 
 def test_checkpoint_resume_is_bit_identical():
