@@ -235,7 +235,7 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
         idx = np.linspace(0, n - 1, m).astype(np.int64)
         sel = __import__("torch").as_tensor(idx, device=a["st"].device)
         st = snapshot(a["st"], heads=sel)
-        ocfg = ocfg_of(a["cfg"]).replace(batch=m, heads=1)
+        ocfg = ocfg_of(a["cfg"], step=a["st"].step_index).replace(batch=m, heads=1)
         samples.append((a, ocfg, st, sel))
 
     def run(steps):

@@ -54,7 +54,7 @@ enum { RND_RNE = 0, RND_BDR = 1, RND_DITHER = 2 };
 
 // Golden-ratio Weyl dither: 2^32 (sqrt(5)-1)/2, truncated.  The offset of
 // sequence position i is frac(i * 0.618...) = ((i * kWeyl) mod 2^32) / 2^32,
-// used with 23 bits: the float 1 + u is 0x3F800000 | (w >> 9).
+// used with 23 bits: the float 1 + u is 0x3F800000 | (w >> 9), one v_alignbit.
 constexpr uint32_t kWeyl = 0x9E3779B9u;
 
 // 1.5 * 2^23: adding it to |y| < 2^22 with one rounding leaves
@@ -629,8 +629,8 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
         // floor(z + u) with the Weyl offsets of elements 8b .. 8b+7
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          e[i] = __uint_as_float(0x3F800000u | ((dbase + (uint32_t)(8 * b + i) * kWeyl) >> 9));
+        for (int i = 0; i < 8; ++i)   // ({0x7F, w} >> 9) = 0x3F800000 | (w >> 9): the float 1 + u
+          e[i] = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, dbase + (uint32_t)(8 * b + i) * kWeyl, 9));
         fma_add_rd8(t, stb, inv, e, F::MQ - 1.f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], F::MQ - F::QMAX, F::MQ + F::QMAX);

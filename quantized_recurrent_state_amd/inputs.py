@@ -21,7 +21,7 @@ import torch
 
 # numeric values of the library's enumerations
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
-ROUND_RNE, ROUND_BDR = 0, 1
+ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
 DECAY_SCALAR, DECAY_DIAG = 0, 1
 
 RECIPES = ("la", "gla", "gdn", "mamba2")
@@ -179,3 +179,23 @@ WORKLOADS = {
                              tuple(range(4, 24)))),
                         shared_inputs=False),
 }
+
+
+def _stack24_variant(key: str, name: str, rounding: int, int4_group: int) -> Workload:
+    base = WORKLOADS["stack24"]
+    return Workload(name, base.recipe, base.batch, base.heads, base.dk, base.dv, base.delta,
+                    base.decay, base.steps, base.warmup,
+                    (Arm("layers0-3-int8g64", 8, 64, POLICY_PERSISTENT, rounding, tuple(range(0, 4))),
+                     Arm(f"layers4-23-int4g{int4_group}", 4, int4_group, POLICY_PERSISTENT, rounding,
+                         tuple(range(4, 24)))),
+                    shared_inputs=False)
+
+
+# The same stack with the other roundings, and with 16-element INT4 groups
+# (INT4 + one fp32 scale per 16 elements: 6 bits per element, 5.33x below fp32).
+WORKLOADS["stack24-rne"] = _stack24_variant(
+    "stack24-rne", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-rne", ROUND_RNE, 32)
+WORKLOADS["stack24-dither"] = _stack24_variant(
+    "stack24-dither", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-dither", ROUND_DITHER, 32)
+WORKLOADS["stack24-g16"] = _stack24_variant(
+    "stack24-g16", "gdn24-512x32-128x128-mixed-int8g64-int4g16-persistent-bdr", ROUND_BDR, 16)
