@@ -52,7 +52,7 @@ def build(force: bool = False) -> str:
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "heads", "dk", "dv", "bits", "group", "policy", "rounding", "delta",
-                 "decay")] + [("step", ctypes.c_int64)]
+                 "decay", "lrb_rank")] + [("step", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
@@ -77,10 +77,13 @@ def lib():
             L.lsqo_run.argtypes = [cfgp, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_int32]
             L.lsqo_calibrate.argtypes = [cfgp, P, P, P, P, P]
+            L.lsqo_step_lrb.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P,
+                                        ctypes.POINTER(_Stats), P, P]
             L.lsqo_dequantize.argtypes = [cfgp, P, P, P]
             L.lsqo_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
             L.lsqo_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
             for f in (L.lsqo_check_config, L.lsqo_step, L.lsqo_step_trace, L.lsqo_run, L.lsqo_calibrate,
+                      L.lsqo_step_lrb,
                       L.lsqo_dequantize, L.lsqo_pack, L.lsqo_unpack):
                 f.restype = ctypes.c_int
             _lib = L
@@ -100,7 +103,8 @@ class OracleConfig:
     rounding: int = ROUND_RNE
     delta: int = 0
     decay: int = DECAY_SCALAR
-    step: int = 0          # sequence position of the (first) step: dithered rounding
+    lrb_rank: int = 0      # Low-Rank Bypass slots (0: off)
+    step: int = 0          # sequence position of the (first) step: dithered rounding, bypass slot
 
     @property
     def n(self) -> int:
@@ -130,10 +134,13 @@ class OracleState:
     scales: np.ndarray | None = None  # f32   [n, Dv, Dk/g]
     ref: np.ndarray | None = None     # f32   [n, Dv, Dk]  (yoked policy)
     f32: np.ndarray | None = None     # f32   [n, Dv, Dk]  (bits == 32)
+    lrb_a: np.ndarray | None = None   # f32   [n, r, Dv]   (Low-Rank Bypass)
+    lrb_b: np.ndarray | None = None   # f32   [n, r, Dk]
 
     def copy(self) -> "OracleState":
         return OracleState(*(None if a is None else a.copy()
-                             for a in (self.codes, self.scales, self.ref, self.f32)))
+                             for a in (self.codes, self.scales, self.ref, self.f32, self.lrb_a,
+                                       self.lrb_b)))
 
 
 def _p(a):
@@ -153,6 +160,9 @@ def zero_state(cfg: OracleConfig) -> OracleState:
                      scales=np.zeros((n, cfg.dv, cfg.ngroups), np.float32))
     if cfg.policy == POLICY_YOKED:
         st.ref = np.zeros((n, cfg.dv, cfg.dk), np.float32)
+    if cfg.lrb_rank > 0:
+        st.lrb_a = np.zeros((n, cfg.lrb_rank, cfg.dv), np.float32)
+        st.lrb_b = np.zeros((n, cfg.lrb_rank, cfg.dk), np.float32)
     return st
 
 
@@ -192,6 +202,16 @@ def step(cfg: OracleConfig, st: OracleState, q, k, v, alpha, beta, stats: dict |
         y = np.zeros((cfg.n, cfg.dv, cfg.dk), np.float64)
         yp = np.zeros((cfg.n, cfg.dv, cfg.dk), np.float64)
         trace["y"], trace["yp"] = y, yp
+    if cfg.lrb_rank > 0:
+        rc = lib().lsqo_step_lrb(ctypes.byref(cfg.c()), _p(st.codes), _p(st.scales), _p(st.lrb_a),
+                                 _p(st.lrb_b), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o),
+                                 ctypes.byref(s), _p(y), _p(yp))
+        if rc:
+            raise RuntimeError("oracle bypass step failed")
+        if stats is not None:
+            stats["clamped"] = stats.get("clamped", 0) + s.clamped
+            stats["bdr_fired"] = stats.get("bdr_fired", 0) + s.bdr_fired
+        return o, None
     rc = lib().lsqo_step_trace(ctypes.byref(cfg.c()), _p(st.codes), _p(st.scales), _p(st.ref),
                                _p(st.f32), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o),
                                _p(o_ref), ctypes.byref(s), _p(y), _p(yp))

@@ -51,6 +51,7 @@ int lsqo_check_config(const lsqo_config* cfg) {
   if (cfg->rounding != LSQO_ROUND_RNE && cfg->rounding != LSQO_ROUND_BDR &&
       cfg->rounding != LSQO_ROUND_DITHER)
     return -1;
+  if (cfg->lrb_rank < 0) return -1;
   return 0;
 }
 
@@ -317,6 +318,160 @@ int lsqo_run(const lsqo_config* cfg, int32_t H, int8_t* codes, float* scales, fl
   }
   free(jobs);
   free(th);
+  return 0;
+}
+
+/* Requantise one group of a row from the fp32 values x (S_t, or the merged
+ * X), the decayed pre-write values sp and the update signs sig (+-1, 0 for
+ * none), under the configuration's rounding; returns the number of codes
+ * changed by directional rounding.  Shared by the bypass step. */
+static int64_t requantise_group(const lsqo_config* cfg, int r, int c0, int c1, const float* x,
+                                const float* sp, const int* sig, float inv, int8_t* C,
+                                lsqo_stats* stats, double* y_row, double* yp_row) {
+  const int qm = qmax_of(cfg->bits);
+  int64_t fired = 0;
+  for (int c = c0; c < c1; ++c) {
+    const double y = (double)x[c] * (double)inv;   /* exact */
+    const double yp = (double)sp[c] * (double)inv; /* exact */
+    if (y_row) { y_row[c] = y; yp_row[c] = yp; }
+    double q0;
+    if (cfg->rounding == LSQO_ROUND_DITHER) {
+      const double u = weyl_dither(cfg->step, cfg->dv, cfg->dk, r, c);
+      const double fy = floor(y);
+      q0 = fy + ((y - fy >= 1.0 - u) ? 1.0 : 0.0);
+      if (yp_row) yp_row[c] = u;
+    } else {
+      q0 = round_half_even(y);
+    }
+    double q1 = clampd(q0, -qm, qm);
+    if (q1 != q0) stats->clamped++;
+    double q2 = q1;
+    if (cfg->rounding == LSQO_ROUND_BDR && sig[c] != 0) {
+      const int sigma = sig[c];
+      if ((sigma > 0 && q1 < yp) || (sigma < 0 && q1 > yp)) {
+        q2 = clampd(q1 + sigma, -qm, qm);
+        if (q2 != q1) fired++;
+      }
+    }
+    C[c] = (int8_t)q2;
+  }
+  stats->bdr_fired += fired;
+  return fired;
+}
+
+int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* lrb_a,
+                  float* lrb_b, const float* q, const float* k, const float* v,
+                  const float* alpha, const float* beta, float* o, lsqo_stats* stats,
+                  double* y_out, double* yp_out) {
+  if (lsqo_check_config(cfg) || cfg->bits == 32 || cfg->lrb_rank < 1) return -1;
+  if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT) return -1;
+  if ((y_out == NULL) != (yp_out == NULL)) return -1;
+  const int dk = cfg->dk, dv = cfg->dv, R = cfg->lrb_rank;
+  const int diag = cfg->decay == LSQO_DECAY_DIAG;
+  const int g = cfg->group, ng = dk / g, qm = qmax_of(cfg->bits);
+  const int n_used = (int)(cfg->step % R);   /* filled slots before this step */
+  const int merge = n_used == R - 1;
+  const int64_t nh = (int64_t)cfg->batch * cfg->heads;
+  lsqo_stats st = {0, 0};
+  float* sp = (float*)malloc(sizeof(float) * (size_t)dk);
+  float* x = (float*)malloc(sizeof(float) * (size_t)dk);
+  int* sig = (int*)malloc(sizeof(int) * (size_t)dk);
+  double* bk = (double*)malloc(sizeof(double) * (size_t)R);
+  double* bq = (double*)malloc(sizeof(double) * (size_t)R);
+  for (int64_t h = 0; h < nh; ++h) {
+    const float* qh = q + h * dk;
+    const float* kh = k + h * dk;
+    const float* ah = alpha + (diag ? h * dk : h);
+    float* A = lrb_a + h * (int64_t)R * dv;   /* A[j*dv + i] = a_j[i] */
+    float* Bv = lrb_b + h * (int64_t)R * dk;  /* Bv[j*dk + c] = b_j[c] */
+    /* decay the buffer with the state: B' = B Lambda_t */
+    for (int j = 0; j < n_used; ++j) {
+      if (diag) {
+        for (int c = 0; c < dk; ++c) Bv[j * dk + c] = Bv[j * dk + c] * ah[c];
+      } else {
+        for (int i = 0; i < dv; ++i) A[j * dv + i] = A[j * dv + i] * ah[0];
+      }
+    }
+    /* per-slot projections b_j . k and b_j . q */
+    for (int j = 0; j < n_used; ++j) {
+      double s1 = 0.0, s2 = 0.0;
+      for (int c = 0; c < dk; ++c) {
+        s1 += (double)Bv[j * dk + c] * (double)kh[c];
+        s2 += (double)Bv[j * dk + c] * (double)qh[c];
+      }
+      bk[j] = s1;
+      bq[j] = s2;
+    }
+    double kq = 0.0;
+    for (int c = 0; c < dk; ++c) kq += (double)kh[c] * (double)qh[c];
+    /* the new slot holds k */
+    for (int c = 0; c < dk; ++c) Bv[n_used * dk + c] = kh[c];
+
+    for (int i = 0; i < dv; ++i) {
+      int8_t* C = codes + (h * dv + i) * (int64_t)dk;
+      float* s = scales + (h * dv + i) * (int64_t)ng;
+      for (int c = 0; c < dk; ++c) {
+        float a = diag ? ah[c] : ah[0];
+        float m = s[c / g] * a;
+        sp[c] = (float)C[c] * m;
+      }
+      /* delta projection on the effective state S' + B' */
+      float u = 0.0f;
+      if (cfg->delta) {
+        double acc = 0.0;
+        for (int c = 0; c < dk; ++c) acc += (double)sp[c] * (double)kh[c];
+        for (int j = 0; j < n_used; ++j) acc += (double)A[j * dv + i] * bk[j];
+        u = (float)acc;
+      }
+      const float w = beta[h] * (v[h * dv + i] - u);
+      A[n_used * dv + i] = w;   /* slot n: the write w k^T */
+      /* readout from S' + B' + w k^T */
+      double oo = 0.0;
+      for (int c = 0; c < dk; ++c) oo += (double)sp[c] * (double)qh[c];
+      for (int j = 0; j < n_used; ++j) oo += (double)A[j * dv + i] * bq[j];
+      oo += (double)w * kq;
+      o[h * dv + i] = (float)oo;
+      /* the value to requantise: the merged X on a merge step, else S' */
+      for (int c = 0; c < dk; ++c) {
+        float xv = sp[c], uv = 0.0f;   /* merged value, and the buffer's own value */
+        if (merge) {
+          for (int j = 0; j <= n_used; ++j) {
+            xv = fmaf(A[j * dv + i], Bv[j * dk + c], xv);
+            uv = fmaf(A[j * dv + i], Bv[j * dk + c], uv);
+          }
+        }
+        x[c] = xv;
+        sig[c] = (uv > 0.0f) - (uv < 0.0f);   /* direction of the accumulated update */
+      }
+      for (int gi = 0; gi < ng; ++gi) {
+        float snew;
+        if (cfg->policy == LSQO_POLICY_PERSISTENT) {
+          snew = s[gi];
+        } else {
+          float amax = 0.0f;
+          for (int c = gi * g; c < (gi + 1) * g; ++c) {
+            float av = fabsf(x[c]);
+            if (av > amax) amax = av;
+          }
+          snew = amax / (float)qm;
+        }
+        const float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
+        requantise_group(cfg, i, gi * g, (gi + 1) * g, x, sp, sig, inv, C, &st,
+                         y_out ? y_out + (h * dv + i) * (int64_t)dk : NULL,
+                         yp_out ? yp_out + (h * dv + i) * (int64_t)dk : NULL);
+        s[gi] = snew;
+      }
+    }
+  }
+  free(sp);
+  free(x);
+  free(sig);
+  free(bk);
+  free(bq);
+  if (stats) {
+    stats->clamped += st.clamped;
+    stats->bdr_fired += st.bdr_fired;
+  }
   return 0;
 }
 

@@ -35,6 +35,22 @@
  *    to 23 bits (u = (w >> 9) * 2^-23), i = step * Dv * Dk + r * Dk + c the
  *    element's position in one sequence that runs through the head's state
  *    row by row, step after step (i taken mod 2^32).
+ *  - "Preserving Updates in Low-Bit Recurrent State Quantization" (abstract):
+ *    Low-Rank Bypass accumulates small updates in a compact low-rank buffer
+ *    and periodically merges its sufficiently large elements into the state.
+ *    Rank, period, threshold and precision are unstated; the reading
+ *    implemented here (lsqo_step_lrb): an fp32 buffer of r rank-one slots
+ *    (a_j in R^Dv, b_j in R^Dk), B = sum_j a_j b_j^T, decayed with the state
+ *    (scalar decay scales a_j, diagonal decay scales b_j, one fp32 product per
+ *    step); each step's write w k^T goes into the next slot instead of into the
+ *    quantised state, the delta projection and the readout see S' + B; every
+ *    r-th step (slot r-1 written) the buffer is merged: X = S' + B built by fmas
+ *    in slot order, requantised under the handle's scale policy and rounding
+ *    (directional rounding takes as the update's sign the sign of the buffer
+ *    value U = sum_j a_j b_j, itself built by fmas in slot order from 0), and
+ *    the buffer is emptied: elements whose code changes are the merged
+ *    "sufficiently large" ones, the rest of the buffer is dropped.  Between
+ *    merges the state is requantised from S' alone.
  *
  * State layout used by the oracle (unpacked, host memory, heads = batch*heads):
  *   codes  int8  [heads][Dv][Dk]        signed codes in [-qmax, qmax]
@@ -66,7 +82,9 @@ typedef struct {
   int32_t rounding; /* LSQO_ROUND_* */
   int32_t delta;    /* 0: linear write, 1: delta-rule correction */
   int32_t decay;    /* LSQO_DECAY_* */
-  int64_t step;     /* sequence position of the (first) step: dithered rounding */
+  int32_t lrb_rank; /* Low-Rank Bypass slots r (0: off; lsqo_step_lrb only) */
+  int64_t step;     /* sequence position of the (first) step: dithered rounding,
+                       and the bypass slot (step mod r) */
 } lsqo_config;
 
 /* counters filled by a step (nullable): element-steps whose code was clamped
@@ -99,6 +117,17 @@ int lsqo_step_trace(const lsqo_config* cfg, int8_t* codes, float* scales, float*
 int lsqo_run(const lsqo_config* cfg, int32_t H, int8_t* codes, float* scales, float* ref,
              float* f32, const float* q, const float* k, const float* v, const float* alpha,
              const float* beta, float* o, float* o_ref, int32_t nthreads);
+
+/* One decode step with Low-Rank Bypass (cfg->lrb_rank = r >= 1; dynamic or
+ * persistent policy; RNE, BDR or dithered rounding; bits 4 or 8).  Buffer
+ * layout: lrb_a [heads][r][Dv], lrb_b [heads][r][Dk] fp32; slots 0 .. n-1
+ * hold the buffer before the step, n = step mod r.  The step writes slot n
+ * and, when n == r-1, merges (see the header note).  trace as lsqo_step_trace
+ * (y_out: X*inv; yp_out: S'*inv, or the dither offset). */
+int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* lrb_a,
+                  float* lrb_b, const float* q, const float* k, const float* v,
+                  const float* alpha, const float* beta, float* o, lsqo_stats* stats,
+                  double* y_out, double* yp_out);
 
 /* Quantise an fp32 state S [heads][Dv][Dk] into this configuration: one scale
  * per group from the group's absolute maximum, codes by round-to-nearest-even
