@@ -59,6 +59,25 @@
  *   scales [heads][Dv][Dk/group] fp32, one per contiguous group along Dk.
  *   ref    [heads][Dv][Dk] fp32, the yoked policy's reference state.
  *   f32    [heads][Dv][Dk] fp32, the state of the unquantised mode (bits 32).
+ *   lrb    Low-Rank Bypass buffer (lrb_rank = r > 0), fp32: a [heads][r][Dv]
+ *          followed by b [heads][2][r][Dk] (copy 1 used by diagonal decay).
+ *
+ * Low-Rank Bypass ("Preserving Updates in Low-Bit Recurrent State
+ * Quantization", abstract: small updates accumulate in a compact low-rank
+ * buffer whose sufficiently large elements are merged into the state
+ * periodically; rank, period and threshold are not given there).  This
+ * library's reading: slot j holds a_j [Dv], b_j [Dk], B = sum_j a_j b_j^T;
+ * at step t, n = t mod r slots are filled (the handle's step index t).  The
+ * buffer decays with the state (scalar decay: a_j = fl(alpha a_j); diagonal:
+ * b_j = fl(b_j alpha)); u and o are taken from S' + B (o also includes the
+ * new write); the write fills slot n (a_n = w, b_n = k) instead of entering
+ * the quantised state, which is requantised from S' alone; when n = r-1 the
+ * step merges instead: X = S' then X = fma(a_j, b_j, X) for j = 0..n in slot
+ * order, the scale policy and rounding applied to X (BDR's update sign is the
+ * sign of U built the same way from 0), and the buffer empties.  b is read from
+ * copy t mod 2 and written to copy (t+1) mod 2 under diagonal decay (copy 0
+ * only under scalar decay).  Supported: bits 4/8, DYNAMIC or PERSISTENT,
+ * groups of 32 or more, r <= 8; the buffer starts as lsq_state_zero leaves it.
  * Inputs per step: q, k [heads][Dk]; v [heads][Dv]; alpha [heads] (scalar
  * decay) or [heads][Dk] (diagonal); beta [heads].  Output o [heads][Dv];
  * o_ref [heads][Dv] (yoked only, nullable).
@@ -114,6 +133,7 @@ typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
 typedef struct {
   int32_t batch, heads, dk, dv;
   int32_t bits, group, policy, rounding, delta, decay;
+  int32_t lrb_rank;   /* Low-Rank Bypass slots r, 0 (off) to 8; see below */
 } lsq_config;
 
 /* Caller-owned device buffers and their capacities in bytes.  Buffers the
@@ -123,6 +143,7 @@ typedef struct {
   float* scales; size_t scales_bytes;
   float* ref;    size_t ref_bytes;
   float* f32;    size_t f32_bytes;
+  float* lrb;    size_t lrb_bytes;    /* Low-Rank Bypass buffer (lrb_rank > 0) */
 } lsq_buffers;
 
 typedef struct lsq_state lsq_state;
@@ -130,7 +151,7 @@ typedef struct lsq_state lsq_state;
 /* Byte sizes of the state buffers a configuration needs (0 when unused).
  * Host only.  Any output pointer may be NULL. */
 lsq_status lsq_state_sizes(const lsq_config* cfg, size_t* codes_bytes, size_t* scales_bytes,
-                           size_t* ref_bytes, size_t* f32_bytes);
+                           size_t* ref_bytes, size_t* f32_bytes, size_t* lrb_bytes);
 
 /* Create a handle that binds the caller's buffers.  Allocates only the host
  * handle.  Checks: valid config, non-null and 16-byte aligned buffers for

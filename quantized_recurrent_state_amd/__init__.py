@@ -37,6 +37,7 @@ class LsqConfig:
     rounding: int = ROUND_RNE
     delta: int = 0
     decay: int = DECAY_SCALAR
+    lrb_rank: int = 0       # Low-Rank Bypass slots (0: off)
 
     @property
     def n(self) -> int:
@@ -57,21 +58,22 @@ def _ptr(t) -> int | None:
     return None if t is None else int(t.data_ptr())
 
 
-def lsq_state_sizes(cfg: LsqConfig) -> tuple[int, int, int, int]:
-    """(codes, scales, ref, f32) byte sizes of the state buffers."""
+def lsq_state_sizes(cfg: LsqConfig) -> tuple[int, int, int, int, int]:
+    """(codes, scales, ref, f32, lrb) byte sizes of the state buffers."""
     L = _lib.load()
-    out = [ctypes.c_size_t(0) for _ in range(4)]
+    out = [ctypes.c_size_t(0) for _ in range(5)]
     _lib.check(L.lsq_state_sizes(ctypes.byref(cfg.c()), *map(ctypes.byref, out)),
                "lsq_state_sizes")
     return tuple(int(x.value) for x in out)
 
 
-def lsq_state_alloc(cfg: LsqConfig, codes=None, scales=None, ref=None, f32=None) -> int:
+def lsq_state_alloc(cfg: LsqConfig, codes=None, scales=None, ref=None, f32=None,
+                    lrb=None) -> int:
     """Bind caller-owned device tensors to a new handle (returns the handle)."""
     L = _lib.load()
     nb = lambda t: 0 if t is None else t.numel() * t.element_size()
     bufs = _lib.lsq_buffers(_ptr(codes), nb(codes), _ptr(scales), nb(scales), _ptr(ref), nb(ref),
-                            _ptr(f32), nb(f32))
+                            _ptr(f32), nb(f32), _ptr(lrb), nb(lrb))
     h = ctypes.c_void_p()
     _lib.check(L.lsq_state_alloc(ctypes.byref(cfg.c()), ctypes.byref(bufs), ctypes.byref(h)),
                "lsq_state_alloc")
@@ -133,9 +135,9 @@ class LsqState:
         import torch
         self.cfg = cfg
         self.device = torch.device(device)
-        _, _, n_ref, n_f32 = lsq_state_sizes(cfg)
+        _, _, n_ref, n_f32, n_lrb = lsq_state_sizes(cfg)
         n, dv, dk = cfg.n, cfg.dv, cfg.dk
-        self.codes = self.scales = self.ref = self.f32 = None
+        self.codes = self.scales = self.ref = self.f32 = self.lrb = None
         if cfg.bits != 32:
             self.codes = torch.empty((n, dv, dk * cfg.bits // 8), dtype=torch.uint8,
                                      device=self.device)
@@ -145,7 +147,25 @@ class LsqState:
             self.ref = torch.empty((n, dv, dk), dtype=torch.float32, device=self.device)
         if cfg.bits == 32:
             self.f32 = torch.empty((n, dv, dk), dtype=torch.float32, device=self.device)
-        self.handle = lsq_state_alloc(cfg, self.codes, self.scales, self.ref, self.f32)
+        if n_lrb:
+            self.lrb = torch.empty(n_lrb // 4, dtype=torch.float32, device=self.device)
+        self.handle = lsq_state_alloc(cfg, self.codes, self.scales, self.ref, self.f32, self.lrb)
+
+    @property
+    def lrb_a(self):
+        """Bypass slots a: view [n, r, Dv] of the buffer (None without bypass)."""
+        if self.lrb is None:
+            return None
+        c = self.cfg
+        return self.lrb[: c.n * c.lrb_rank * c.dv].view(c.n, c.lrb_rank, c.dv)
+
+    @property
+    def lrb_b(self):
+        """Bypass slots b: view [n, 2, r, Dk] (copy 1 used by diagonal decay)."""
+        if self.lrb is None:
+            return None
+        c = self.cfg
+        return self.lrb[c.n * c.lrb_rank * c.dv:].view(c.n, 2, c.lrb_rank, c.dk)
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -21,14 +21,15 @@ STATUS_NAMES = {0: "LSQ_OK", 1: "LSQ_ERR_INVALID_ARG", 2: "LSQ_ERR_UNSUPPORTED",
 class lsq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "heads", "dk", "dv", "bits", "group", "policy", "rounding", "delta",
-                 "decay")]
+                 "decay", "lrb_rank")]
 
 
 class lsq_buffers(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("codes_bytes", ctypes.c_size_t),
                 ("scales", ctypes.c_void_p), ("scales_bytes", ctypes.c_size_t),
                 ("ref", ctypes.c_void_p), ("ref_bytes", ctypes.c_size_t),
-                ("f32", ctypes.c_void_p), ("f32_bytes", ctypes.c_size_t)]
+                ("f32", ctypes.c_void_p), ("f32_bytes", ctypes.c_size_t),
+                ("lrb", ctypes.c_void_p), ("lrb_bytes", ctypes.c_size_t)]
 
 
 class LsqError(RuntimeError):
@@ -53,7 +54,7 @@ def load() -> ctypes.CDLL:
     cfgp = ctypes.POINTER(lsq_config)
     sig = {
         "lsq_state_sizes": [cfgp, ctypes.POINTER(S), ctypes.POINTER(S), ctypes.POINTER(S),
-                            ctypes.POINTER(S)],
+                            ctypes.POINTER(S), ctypes.POINTER(S)],
         "lsq_state_alloc": [cfgp, ctypes.POINTER(lsq_buffers), ctypes.POINTER(P)],
         "lsq_state_free": [P],
         "lsq_state_config": [P, cfgp],

@@ -17,6 +17,7 @@ struct lsq_state {
   float* scales;
   float* ref;
   float* f32;
+  float* lrb;
   int32_t calibrated;
   int64_t step;          // sequence position of the next step (dithered rounding)
 };
@@ -78,6 +79,15 @@ lsq_status check_config(const lsq_config* c) {
                   "group %d: this build needs a power-of-two group of at least %d elements",
                   c->group, min_group);
   }
+  if (c->lrb_rank < 0 || c->lrb_rank > 8)
+    return fail(LSQ_ERR_INVALID_ARG, "lrb_rank must be 0 to 8");
+  if (c->lrb_rank > 0) {
+    if (c->bits == 32) return fail(LSQ_ERR_INVALID_ARG, "the bypass applies to a quantised state");
+    if (c->policy != LSQ_POLICY_DYNAMIC && c->policy != LSQ_POLICY_PERSISTENT)
+      return fail(LSQ_ERR_UNSUPPORTED, "the bypass supports the DYNAMIC and PERSISTENT policies");
+    if (c->group < 32)
+      return fail(LSQ_ERR_UNSUPPORTED, "the bypass needs groups of 32 or more elements");
+  }
   const lsq::Geometry g = lsq::geometry(c->bits, c->dk);
   const int64_t iters = (c->dv + g.rows_per_iter - 1) / g.rows_per_iter;
   if (n_heads(*c) * iters > INT32_MAX / 2)
@@ -85,16 +95,19 @@ lsq_status check_config(const lsq_config* c) {
   return ok();
 }
 
-void sizes_of(const lsq_config& c, size_t* codes, size_t* scales, size_t* ref, size_t* f32) {
+constexpr int kBuffers = 5;   // codes, scales, ref, f32, lrb
+
+void sizes_of(const lsq_config& c, size_t (&sz)[kBuffers]) {
   const size_t elems = (size_t)n_heads(c) * c.dv * c.dk;
-  *codes = *scales = *ref = *f32 = 0;
+  for (size_t& x : sz) x = 0;
   if (c.bits == 32) {
-    *f32 = elems * 4;
+    sz[3] = elems * 4;
     return;
   }
-  *codes = elems * c.bits / 8;
-  *scales = (size_t)n_heads(c) * c.dv * (c.dk / c.group) * 4;
-  if (c.policy == LSQ_POLICY_YOKED) *ref = elems * 4;
+  sz[0] = elems * c.bits / 8;
+  sz[1] = (size_t)n_heads(c) * c.dv * (c.dk / c.group) * 4;
+  if (c.policy == LSQ_POLICY_YOKED) sz[2] = elems * 4;
+  if (c.lrb_rank > 0) sz[4] = (size_t)n_heads(c) * c.lrb_rank * (c.dv + 2 * (size_t)c.dk) * 4;
 }
 
 // Launch geometry: one wave per (head, slice of nit row-iterations); slices
@@ -147,7 +160,17 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
   a.dither_base = (uint32_t)((uint64_t)st->step * (uint64_t)c.dv * (uint64_t)c.dk) * kWeyl;
   a.dither_row = (uint32_t)c.dk * kWeyl;
   hipError_t e;
-  if (c.bits == 32)
+  if (c.lrb_rank > 0) {
+    const int64_t r = c.lrb_rank;
+    a.lrb_a = st->lrb;
+    a.lrb_b = st->lrb + n_heads(c) * r * c.dv;
+    a.lrb_rank = c.lrb_rank;
+    a.lrb_used = (int32_t)(st->step % r);
+    a.lrb_merge = a.lrb_used == c.lrb_rank - 1;
+    a.lrb_cin = (c.decay == LSQ_DECAY_DIAG) ? (int32_t)(st->step & 1) : 0;
+    a.lrb_cout = (c.decay == LSQ_DECAY_DIAG) ? (int32_t)((st->step + 1) & 1) : 0;
+    e = lsq::launch_lrb_step(a, c.bits, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
+  } else if (c.bits == 32)
     e = lsq::launch_step_f32(a, c.dk, c.delta, c.decay, stream);
   else if (c.bits == 4)
     e = lsq::launch_step_q4(a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
@@ -163,15 +186,14 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
 extern "C" {
 
 lsq_status lsq_state_sizes(const lsq_config* cfg, size_t* codes_bytes, size_t* scales_bytes,
-                           size_t* ref_bytes, size_t* f32_bytes) {
+                           size_t* ref_bytes, size_t* f32_bytes, size_t* lrb_bytes) {
   lsq_status s = check_config(cfg);
   if (s != LSQ_OK) return s;
-  size_t a, b, c, d;
-  sizes_of(*cfg, &a, &b, &c, &d);
-  if (codes_bytes) *codes_bytes = a;
-  if (scales_bytes) *scales_bytes = b;
-  if (ref_bytes) *ref_bytes = c;
-  if (f32_bytes) *f32_bytes = d;
+  size_t sz[kBuffers];
+  sizes_of(*cfg, sz);
+  size_t* out[kBuffers] = {codes_bytes, scales_bytes, ref_bytes, f32_bytes, lrb_bytes};
+  for (int i = 0; i < kBuffers; ++i)
+    if (out[i]) *out[i] = sz[i];
   return ok();
 }
 
@@ -181,12 +203,13 @@ lsq_status lsq_state_alloc(const lsq_config* cfg, const lsq_buffers* bufs, lsq_s
   lsq_status s = check_config(cfg);
   if (s != LSQ_OK) return s;
   if (!bufs) return fail(LSQ_ERR_INVALID_ARG, "buffers are null");
-  size_t need[4];
-  sizes_of(*cfg, &need[0], &need[1], &need[2], &need[3]);
-  const void* ptr[4] = {bufs->codes, bufs->scales, bufs->ref, bufs->f32};
-  const size_t cap[4] = {bufs->codes_bytes, bufs->scales_bytes, bufs->ref_bytes, bufs->f32_bytes};
-  static const char* names[4] = {"codes", "scales", "ref", "f32"};
-  for (int i = 0; i < 4; ++i) {
+  size_t need[kBuffers];
+  sizes_of(*cfg, need);
+  const void* ptr[kBuffers] = {bufs->codes, bufs->scales, bufs->ref, bufs->f32, bufs->lrb};
+  const size_t cap[kBuffers] = {bufs->codes_bytes, bufs->scales_bytes, bufs->ref_bytes,
+                                bufs->f32_bytes, bufs->lrb_bytes};
+  static const char* names[kBuffers] = {"codes", "scales", "ref", "f32", "lrb"};
+  for (int i = 0; i < kBuffers; ++i) {
     if (need[i] == 0) continue;
     if (!ptr[i]) return fail(LSQ_ERR_INVALID_ARG, "%s buffer is null", names[i]);
     if (!aligned16(ptr[i])) return fail(LSQ_ERR_INVALID_ARG, "%s buffer is not 16-byte aligned", names[i]);
@@ -201,6 +224,7 @@ lsq_status lsq_state_alloc(const lsq_config* cfg, const lsq_buffers* bufs, lsq_s
   st->scales = need[1] ? bufs->scales : nullptr;
   st->ref = need[2] ? bufs->ref : nullptr;
   st->f32 = need[3] ? bufs->f32 : nullptr;
+  st->lrb = need[4] ? bufs->lrb : nullptr;
   st->calibrated = 0;
   st->step = 0;
   *out = st;
@@ -217,11 +241,11 @@ lsq_status lsq_state_config(const lsq_state* st, lsq_config* out) {
 
 lsq_status lsq_state_zero(lsq_state* st, void* stream) {
   if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
-  size_t need[4];
-  sizes_of(st->cfg, &need[0], &need[1], &need[2], &need[3]);
-  void* ptr[4] = {st->codes, st->scales, st->ref, st->f32};
+  size_t need[kBuffers];
+  sizes_of(st->cfg, need);
+  void* ptr[kBuffers] = {st->codes, st->scales, st->ref, st->f32, st->lrb};
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kBuffers; ++i) {
     if (!need[i]) continue;
     lsq_status s = hip_status(lsq::launch_fill_zero(ptr[i], need[i], hs), "zero fill");
     if (s != LSQ_OK) return s;

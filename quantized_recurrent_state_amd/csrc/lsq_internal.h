@@ -31,6 +31,13 @@ struct StepArgs {
   // dither_base + r * dither_row + c * 0x9E3779B9 (mod 2^32)
   uint32_t dither_base;  // (step * dv * dk) * 0x9E3779B9 mod 2^32
   uint32_t dither_row;   // dk * 0x9E3779B9 mod 2^32
+  // Low-Rank Bypass (lrb_rank > 0): a [n][r][dv], b [n][2][r][dk]
+  float* lrb_a;
+  float* lrb_b;
+  int32_t lrb_rank;
+  int32_t lrb_used;      // slots filled before this step (step mod r)
+  int32_t lrb_merge;     // 1 when this step fills the last slot and merges
+  int32_t lrb_cin, lrb_cout;  // b copy read / written this step
 };
 
 // Arguments of a calibration launch: quantise an fp32 state into codes/scales.
@@ -59,6 +66,8 @@ hipError_t launch_step_q8(const StepArgs& a, int dk, int policy, int rounding, i
                           hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, int dk, int delta, int diag, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s);
+hipError_t launch_lrb_step(const StepArgs& a, int bits, int dk, int policy, int rounding,
+                           int delta, int diag, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace lsq

@@ -118,12 +118,15 @@ def boundary_distance(y, yp, codes_oracle, rounding):
 
 
 def compare_step(ocfg: OracleConfig, before: OracleState, inputs, gpu_after: OracleState,
-                 gpu_o, gpu_o_ref=None) -> Report:
-    """Run the oracle from the GPU's pre-step state and compare with the GPU's result."""
+                 gpu_o, gpu_o_ref=None, oracle_after: list | None = None) -> Report:
+    """Run the oracle from the GPU's pre-step state and compare with the GPU's result
+    (the oracle's post-step state is appended to ``oracle_after`` when given)."""
     rep = Report()
     st = before.copy()
     trace, stats = {}, {}
     o, o_ref = oracle.step(ocfg, st, *inputs, stats=stats, trace=trace)
+    if oracle_after is not None:
+        oracle_after.append(st)
     rep.max_o_rel = _normwise(np.asarray(gpu_o), o)
     if ocfg.bits == 32:
         rep.max_ref_rel = _normwise(gpu_after.f32, st.f32)

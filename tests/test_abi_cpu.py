@@ -27,13 +27,16 @@ def test_every_declared_symbol_is_exported():
 
 @pytest.mark.parametrize("cfg,want", [
     # INT4 g32 128x128: 64 B codes + 4 scales per row
-    (lsq.LsqConfig(2, 3, 128, 128, 4, 32, lsq.POLICY_PERSISTENT), (6 * 128 * 64, 6 * 128 * 16, 0, 0)),
+    (lsq.LsqConfig(2, 3, 128, 128, 4, 32, lsq.POLICY_PERSISTENT), (6 * 128 * 64, 6 * 128 * 16, 0, 0, 0)),
     # INT8 g64 Dv 64: 128 B codes + 2 scales per row
-    (lsq.LsqConfig(1, 5, 128, 64, 8, 64, lsq.POLICY_DYNAMIC), (5 * 64 * 128, 5 * 64 * 8, 0, 0)),
+    (lsq.LsqConfig(1, 5, 128, 64, 8, 64, lsq.POLICY_DYNAMIC), (5 * 64 * 128, 5 * 64 * 8, 0, 0, 0)),
     # yoked adds the fp32 reference
-    (lsq.LsqConfig(1, 1, 64, 64, 4, 32, lsq.POLICY_YOKED), (64 * 32, 64 * 8, 64 * 64 * 4, 0)),
+    (lsq.LsqConfig(1, 1, 64, 64, 4, 32, lsq.POLICY_YOKED), (64 * 32, 64 * 8, 64 * 64 * 4, 0, 0)),
     # fp32 state
-    (lsq.LsqConfig(1, 2, 64, 32, 32, 1, lsq.POLICY_NONE), (0, 0, 0, 2 * 32 * 64 * 4)),
+    (lsq.LsqConfig(1, 2, 64, 32, 32, 1, lsq.POLICY_NONE), (0, 0, 0, 2 * 32 * 64 * 4, 0)),
+    # bypass: a [n][r][Dv] + b [n][2][r][Dk] fp32
+    (lsq.LsqConfig(1, 2, 128, 64, 4, 32, lsq.POLICY_PERSISTENT, lrb_rank=4),
+     (2 * 64 * 64, 2 * 64 * 16, 0, 0, 2 * 4 * (64 + 2 * 128) * 4)),
 ])
 def test_state_sizes(cfg, want):
     assert lsq.lsq_state_sizes(cfg) == want
@@ -44,7 +47,8 @@ BAD = [
     (dict(policy=lsq.POLICY_NONE), 1), (dict(group=48), 1), (dict(group=0), 1),
     (dict(delta=2), 1), (dict(decay=3), 1), (dict(rounding=7), 1), (dict(batch=-1), 1),
     (dict(dk=96, group=32), 2), (dict(group=8), 2), (dict(bits=8, group=8), 2),
-    (dict(group=24), 1),
+    (dict(group=24), 1), (dict(lrb_rank=9), 1), (dict(lrb_rank=-1), 1),
+    (dict(lrb_rank=2, policy=lsq.POLICY_YOKED), 2), (dict(lrb_rank=2, group=16), 2),
     (dict(dk=256, group=32), 2),
 ]
 
@@ -65,7 +69,7 @@ def _alloc(cfg, codes=FAKE, cb=None, scales=FAKE, sb=None):
     L = _lib.load()
     need = lsq.lsq_state_sizes(cfg)
     bufs = _lib.lsq_buffers(codes, need[0] if cb is None else cb, scales,
-                            need[1] if sb is None else sb, None, 0, None, 0)
+                            need[1] if sb is None else sb, None, 0, None, 0, None, 0)
     h = ctypes.c_void_p()
     st = L.lsq_state_alloc(ctypes.byref(cfg.c()), ctypes.byref(bufs), ctypes.byref(h))
     return st, h.value

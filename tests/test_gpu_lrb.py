@@ -1,0 +1,89 @@
+"""GPU parity of the Low-Rank Bypass step against the CPU oracle.
+
+Teacher-forced as the plain step (tests/parity.py): before every step the
+oracle takes the GPU's codes, scales and bypass slots (a, and the b copy the
+step reads); after it the codes, scales and o are held to the usual bar, and
+the slots the next step will read are compared: decayed slots and the new
+b = k bit for bit, the new a = w (which depends on the delta projection's
+summation order) within 1e-5 of its row's norm.  Runs of 2r+1 steps cover
+two merges and the slot reuse after a merge.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_recurrent_state_amd as lsq
+from quantized_recurrent_state_amd.inputs import gen_steps
+from tests.parity import Report, compare_step, ocfg_of, snapshot, _normwise
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(recipe, n, dk, dv, steps, seed=4):
+    d = gen_steps(recipe, n, dk, dv, [seed], 0, steps, device="cpu")
+    return {k: v.to(DEV) for k, v in d.items()}, {k: v.numpy() for k, v in d.items()}
+
+
+def _run(cfg, steps, recipe, t0=0):
+    R = cfg.lrb_rank
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    if cfg.policy == lsq.POLICY_PERSISTENT:
+        g = torch.Generator(device=DEV).manual_seed(1)
+        st.calibrate(torch.randn(cfg.n, cfg.dv, cfg.dk, device=DEV, generator=g) * 0.3)
+    st.step_index = t0
+    dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, steps)
+    rep = Report()
+    diag = cfg.decay == lsq.DECAY_DIAG
+    for t in range(steps):
+        ti = st.step_index
+        before = snapshot(st)
+        before.lrb_a = st.lrb_a.cpu().numpy().copy()
+        before.lrb_b = st.lrb_b[:, (ti & 1) if diag else 0].cpu().numpy().copy()
+        o = st.step(dg["q"][t], dg["k"][t], dg["v"][t], dg["alpha"][t], dg["beta"][t])
+        after = snapshot(st)
+        ora = []
+        rep.add(compare_step(ocfg_of(cfg, step=ti).replace(lrb_rank=R), before,
+                             tuple(dn[x][t] for x in ("q", "k", "v", "alpha", "beta")), after,
+                             o.cpu().numpy(), oracle_after=ora))
+        n_after = (ti + 1) % R
+        if n_after:
+            want = ora[0]
+            ga = st.lrb_a.cpu().numpy()
+            gb = st.lrb_b[:, ((ti + 1) & 1) if diag else 0].cpu().numpy()
+            used = n_after - 1                     # slots decayed this step
+            assert np.array_equal(ga[:, :used], want.lrb_a[:, :used]), (t, "decayed a")
+            assert np.array_equal(gb[:, :n_after], want.lrb_b[:, :n_after]), (t, "b")
+            assert _normwise(ga[:, used], want.lrb_a[:, used]) <= 1e-5, (t, "new a")
+    return rep
+
+
+COMBOS = [(bits, dk, pol, rnd, dl, dc)
+          for bits in (4, 8)
+          for dk in (128, 64)
+          for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+          for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR, lsq.ROUND_DITHER)
+          for dl in (0, 1)
+          for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc", COMBOS)
+def test_bypass_step_matches_oracle(bits, dk, pol, rnd, dl, dc):
+    R = 3
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=44, bits=bits, group=min(32 if bits == 4 else 64, dk),
+                        policy=pol, rounding=rnd, delta=dl, decay=dc, lrb_rank=R)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run(cfg, 2 * R + 1, recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
+@pytest.mark.parametrize("R", [1, 2, 8])
+def test_bypass_ranks_and_offsets(R):
+    cfg = lsq.LsqConfig(batch=4, heads=4, dk=128, dv=128, bits=4, group=32,
+                        policy=lsq.POLICY_PERSISTENT, rounding=lsq.ROUND_BDR, delta=1,
+                        decay=lsq.DECAY_SCALAR, lrb_rank=R)
+    rep = _run(cfg, R + 3, "gdn", t0=5 * R + 1)     # start mid-period
+    assert rep.ok, str(rep)
