@@ -227,6 +227,8 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
     from tests.parity import ocfg_of, snapshot
 
     threads = max(1, min(16, os.cpu_count() or 1))
+    if any(a["cfg"].lrb_rank > 0 for a in arms):
+        threads = 1                               # the bypass oracle steps one call at a time
     frac = 1.0 / 32                               # sampled share of every arm's heads
     samples = []
     for a in arms:
@@ -235,7 +237,12 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
         idx = np.linspace(0, n - 1, m).astype(np.int64)
         sel = __import__("torch").as_tensor(idx, device=a["st"].device)
         st = snapshot(a["st"], heads=sel)
-        ocfg = ocfg_of(a["cfg"], step=a["st"].step_index).replace(batch=m, heads=1)
+        t_now = a["st"].step_index
+        ocfg = ocfg_of(a["cfg"], step=t_now).replace(batch=m, heads=1, lrb_rank=a["cfg"].lrb_rank)
+        if ocfg.lrb_rank > 0:
+            cin = (t_now & 1) if a["cfg"].decay else 0
+            st.lrb_a = a["st"].lrb_a.index_select(0, sel).cpu().numpy().copy()
+            st.lrb_b = a["st"].lrb_b[:, cin].index_select(0, sel).cpu().numpy().copy()
         samples.append((a, ocfg, st, sel))
 
     def run(steps):
@@ -245,7 +252,13 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
             x = {k: i[k][:steps].index_select(1, sel).cpu().numpy() for k in i}
             s2 = st.copy()
             t0 = time.perf_counter()
-            oracle.run(ocfg, s2, x["q"], x["k"], x["v"], x["alpha"], x["beta"], nthreads=threads)
+            if ocfg.lrb_rank > 0:
+                for t in range(steps):
+                    oracle.step(ocfg.replace(step=ocfg.step + t), s2, x["q"][t], x["k"][t],
+                                x["v"][t], x["alpha"][t], x["beta"][t])
+            else:
+                oracle.run(ocfg, s2, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                           nthreads=threads)
             dt += time.perf_counter() - t0
             total_b += runner.algorithmic_bytes(a["cfg"]) // a["cfg"].n * ocfg.n * steps
             total_hs += ocfg.n * steps

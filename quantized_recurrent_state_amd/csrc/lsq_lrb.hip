@@ -30,7 +30,10 @@ namespace dev {
 
 constexpr int kMaxRank = 8;
 
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG>
+
+// MERGE: this step fills the last slot and merges (a separate instance, so
+// that the other steps carry none of the merge's registers).
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, bool MERGE>
 __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
   using F = Fmt<BITS>;
   constexpr int NW = F::NW;
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
   const int lr = lane / LPR, lc = lane % LPR, col0 = lc * EPL;
   const int gl = a.group / EPL, gi = col0 / a.group;
   const int R = a.lrb_rank, nu = a.lrb_used;   // slots filled before this step
-  const bool merge = a.lrb_merge != 0;
+  constexpr bool merge = MERGE;
 
   __shared__ float4 lds4[4 * WF / 4];
   float* vec = reinterpret_cast<float*>(lds4) + (threadIdx.x >> 6) * WF;
@@ -70,7 +73,10 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
   float* bh_in = a.lrb_b + ((size_t)h * 2 + a.lrb_cin) * R * DK;
   float* bh_out = a.lrb_b + ((size_t)h * 2 + a.lrb_cout) * R * DK;
   float bk[kMaxRank], bq[kMaxRank];
-  for (int j = 0; j < nu; ++j) {
+#pragma unroll
+  for (int j = 0; j < kMaxRank; ++j) {
+    bk[j] = bq[j] = 0.f;
+    if (j >= nu) continue;
     float b[EPL];
     load_f32(b, bh_in + (size_t)j * DK + col0);
     if constexpr (DIAG) {
@@ -102,73 +108,131 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
 
   const size_t row0 = (size_t)h * a.dv;
   float* ah = a.lrb_a + (size_t)h * R * a.dv;   // a_j[i] at ah[j*dv + i]
+  // the next row's codes, scale, v and slots a_j are loaded one row ahead
+  struct RowData {
+    uint32_t x[NW];
+    float s, v;
+    float aj[kMaxRank];
+  };
+  auto row_index = [&](int it) {
+    const int r = (slice * a.nit + it) * RPI + lr;
+    return r < a.dv ? r : a.dv - 1;
+  };
+  auto load_row_data = [&](int it, RowData& d) {
+    const int i = row_index(it);
+    const size_t row = row0 + i;
+    const uint8_t* p = a.codes + row * ROWB + lc * (EPL * BITS / 8);
+#pragma unroll
+    for (int c = 0; c < NW / 4; ++c) {
+      const uint4 w4 = reinterpret_cast<const uint4*>(p)[c];
+      d.x[4 * c] = w4.x; d.x[4 * c + 1] = w4.y; d.x[4 * c + 2] = w4.z; d.x[4 * c + 3] = w4.w;
+    }
+    d.s = a.scales[row * a.ng + gi];
+    d.v = a.v[row];
+#pragma unroll
+    for (int j = 0; j < kMaxRank; ++j) d.aj[j] = (j < nu) ? ah[(size_t)j * a.dv + i] : 0.f;
+  };
+  RowData cur, nxt;
+  load_row_data(0, cur);
   for (int it = 0; it < a.nit; ++it) {
+    if (it + 1 < a.nit) load_row_data(it + 1, nxt);
     const int r = (slice * a.nit + it) * RPI + lr;
     const bool live = r < a.dv;
     const int i = live ? r : a.dv - 1;
     const size_t row = row0 + i;
+    int base = col0;                              // laundered: LDS reads stay in the loop
+    asm volatile("" : "+v"(base));
     // codes -> S' (decay folded into the scale)
     uint32_t x[NW];
-    {
-      const uint8_t* p = a.codes + row * ROWB + lc * (EPL * BITS / 8);
 #pragma unroll
-      for (int c = 0; c < NW / 4; ++c) {
-        const uint4 w4 = reinterpret_cast<const uint4*>(p)[c];
-        x[4 * c] = w4.x ^ F::OFF; x[4 * c + 1] = w4.y ^ F::OFF;
-        x[4 * c + 2] = w4.z ^ F::OFF; x[4 * c + 3] = w4.w ^ F::OFF;
-      }
-    }
-    const float s = a.scales[row * a.ng + gi];
+    for (int c = 0; c < NW; ++c) x[c] = cur.x[c] ^ F::OFF;
+    const float s = cur.s;
     float sp[EPL];
-    unpack_offsets<BITS>(x, sp);
+    if constexpr (DIAG) {
+      unpack_offsets<BITS>(x, sp);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float m = s * (DIAG ? aa[e] : alpha_s);
-      sp[e] = (sp[e] - F::BIAS) * m;
+      for (int b = 0; b < EPL / 8; ++b) {
+        float ab[8];
+        lds_block<DK>(ab, av, base + 8 * b);
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) sp[8 * b + e8] = (sp[8 * b + e8] - F::BIAS) * (s * ab[e8]);
+      }
+    } else {
+      const float m[1] = {s * alpha_s}, mb[1] = {-F::BIAS * (s * alpha_s)};
+      dequant_mix<BITS, 1>(x, m, mb, sp);
     }
     // decayed a'_j of this row
     float ap[kMaxRank];
-    for (int j = 0; j < nu; ++j) {
-      const float aj = ah[(size_t)j * a.dv + i];
-      ap[j] = DIAG ? aj : aj * alpha_s;
-    }
+#pragma unroll
+    for (int j = 0; j < kMaxRank; ++j) ap[j] = DIAG ? cur.aj[j] : cur.aj[j] * alpha_s;
     // delta projection on S' + B', the write coefficient, the readout
     float u = 0.f;
     if constexpr (DELTA) {
       float p = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(sp[e], kk[e], p);
+      for (int b = 0; b < EPL / 8; ++b) {
+        float kb[8];
+        lds_block<DK>(kb, kv, base + 8 * b);
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) p = fmaf(sp[8 * b + e8], kb[e8], p);
+      }
       u = row_sum<LPR>(p);
-      for (int j = 0; j < nu; ++j) u = fmaf(ap[j], bk[j], u);
+#pragma unroll
+      for (int j = 0; j < kMaxRank; ++j)
+        if (j < nu) u = fmaf(ap[j], bk[j], u);
     }
-    const float w = beta * (a.v[row] - u);
+    const float w = beta * (cur.v - u);
     float po = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) po = fmaf(sp[e], qq[e], po);
+    for (int b = 0; b < EPL / 8; ++b) {
+      float qb[8];
+      lds_block<DK>(qb, qv, base + 8 * b);
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) po = fmaf(sp[8 * b + e8], qb[e8], po);
+    }
     float o = row_sum<LPR>(po);
-    for (int j = 0; j < nu; ++j) o = fmaf(ap[j], bq[j], o);
+#pragma unroll
+    for (int j = 0; j < kMaxRank; ++j)
+      if (j < nu) o = fmaf(ap[j], bq[j], o);
     o = fmaf(w, kq, o);
     if (live && lc == 0) a.o[row] = o;
 
-    // the value to requantise: X = S' + B on a merge step, else S'
-    float X[EPL], U[EPL];
+    // the value to requantise: X = S' + B on a merge step, else S' itself; the
+    // buffer's own value U (for the direction of directional rounding)
+    constexpr bool KEEP_U = MERGE && ROUND == RND_BDR;
+    float Xm[MERGE ? EPL : 1], U[KEEP_U ? EPL : 1];
+    if constexpr (MERGE) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) { X[e] = sp[e]; U[e] = 0.f; }
-    if (merge) {
-      for (int j = 0; j < nu; ++j) {
+      for (int e = 0; e < EPL; ++e) {
+        Xm[e] = sp[e];
+        if constexpr (KEEP_U) U[e] = 0.f;
+      }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float bj = bv[j * DK + col0 + e];
-          X[e] = fmaf(ap[j], bj, X[e]);
-          U[e] = fmaf(ap[j], bj, U[e]);
+      for (int jj = 0; jj < kMaxRank; ++jj) {
+        if (jj >= nu) continue;
+#pragma unroll
+        for (int b = 0; b < EPL / 8; ++b) {
+          float bb[8];
+          lds_block<DK>(bb, bv, jj * DK + base + 8 * b);
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) {
+            Xm[8 * b + e8] = fmaf(ap[jj], bb[e8], Xm[8 * b + e8]);
+            if constexpr (KEEP_U) U[8 * b + e8] = fmaf(ap[jj], bb[e8], U[8 * b + e8]);
+          }
         }
       }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        X[e] = fmaf(w, kk[e], X[e]);
-        U[e] = fmaf(w, kk[e], U[e]);
+      for (int b = 0; b < EPL / 8; ++b) {
+        float kb[8];
+        lds_block<DK>(kb, kv, base + 8 * b);
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+          Xm[8 * b + e8] = fmaf(w, kb[e8], Xm[8 * b + e8]);
+          if constexpr (KEEP_U) U[8 * b + e8] = fmaf(w, kb[e8], U[8 * b + e8]);
+        }
       }
     }
+    const float* X = MERGE ? Xm : sp;
     float snew = s;
     if constexpr (POLICY == POL_DYNAMIC) {
       float amax = 0.f;
@@ -195,17 +259,18 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         t[e] = __builtin_amdgcn_fmed3f(fmaf(X[e], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
-      if constexpr (ROUND == RND_BDR) {
-        if (merge) {
+      if constexpr (KEEP_U) {
+        {
           // reversal: the rounded code c1 lies on the far side of y' = S' inv
           // from the buffer's update; move it one step toward the update
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
             const float c1 = t[e] - F::MQ;                     // exact
             const float d = fmaf(sp[e], inv, -c1);             // sign of y' - c1, exact
-            const float sg = (U[e] > 0.f) ? 1.f : ((U[e] < 0.f) ? -1.f : 0.f);
-            if (sg * d > 0.f)
-              t[e] = __builtin_amdgcn_fmed3f(t[e] + sg, F::MQ - F::QMAX, F::MQ + F::QMAX);
+            const bool up = U[e] > 0.f && d > 0.f;
+            const bool dn = U[e] < 0.f && d < 0.f;
+            const float step = up ? 1.f : (dn ? -1.f : 0.f);    // branch-free
+            t[e] = __builtin_amdgcn_fmed3f(t[e] + step, F::MQ - F::QMAX, F::MQ + F::QMAX);
           }
         }
       }
@@ -224,11 +289,14 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
       // the buffer: decayed a'_j (scalar decay) and the new slot a_nu = w
       if (!merge && lc == 0) {
         if constexpr (!DIAG) {
-          for (int j = 0; j < nu; ++j) ah[(size_t)j * a.dv + i] = ap[j];
+#pragma unroll
+          for (int j = 0; j < kMaxRank; ++j)
+            if (j < nu) ah[(size_t)j * a.dv + i] = ap[j];
         }
         ah[(size_t)nu * a.dv + i] = w;
       }
     }
+    cur = nxt;
   }
 }
 
@@ -239,7 +307,10 @@ hipError_t launch_lrb_step(const StepArgs& a, int bits, int dk, int policy, int 
   const dim3 grid((a.total_waves + 3) / 4), block(256);
 #define LSQ_LRB(B, DK, P, RD, D, G)                                                          \
   if (bits == B && dk == DK && policy == P && rounding == RD && delta == D && diag == G) {   \
-    hipLaunchKernelGGL((dev::lrb_step_kernel<B, DK, P, RD, D, G>), grid, block, 0, s, a);   \
+    if (a.lrb_merge)                                                                        \
+      hipLaunchKernelGGL((dev::lrb_step_kernel<B, DK, P, RD, D, G, true>), grid, block, 0, s, a); \
+    else                                                                                    \
+      hipLaunchKernelGGL((dev::lrb_step_kernel<B, DK, P, RD, D, G, false>), grid, block, 0, s, a); \
     return hipGetLastError();                                                               \
   }
 #define LSQ_LRB_DG(B, DK, P, RD) \

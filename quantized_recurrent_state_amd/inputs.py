@@ -127,6 +127,7 @@ class Arm:
     policy: int
     rounding: int
     layers: tuple = (0,)   # layer indices folded into the batch; seeds are per layer
+    lrb_rank: int = 0      # Low-Rank Bypass slots (0: off)
 
 
 @dataclass(frozen=True)
@@ -148,7 +149,7 @@ class Workload:
     def arm_config(self, arm: Arm) -> dict:
         return dict(batch=self.batch * len(arm.layers), heads=self.heads, dk=self.dk, dv=self.dv,
                     bits=arm.bits, group=arm.group, policy=arm.policy, rounding=arm.rounding,
-                    delta=self.delta, decay=self.decay)
+                    delta=self.delta, decay=self.decay, lrb_rank=arm.lrb_rank)
 
 
 WORKLOADS = {
@@ -181,13 +182,15 @@ WORKLOADS = {
 }
 
 
-def _stack24_variant(key: str, name: str, rounding: int, int4_group: int) -> Workload:
+def _stack24_variant(key: str, name: str, rounding: int, int4_group: int,
+                     lrb_rank: int = 0) -> Workload:
     base = WORKLOADS["stack24"]
     return Workload(name, base.recipe, base.batch, base.heads, base.dk, base.dv, base.delta,
                     base.decay, base.steps, base.warmup,
-                    (Arm("layers0-3-int8g64", 8, 64, POLICY_PERSISTENT, rounding, tuple(range(0, 4))),
+                    (Arm("layers0-3-int8g64", 8, 64, POLICY_PERSISTENT, rounding, tuple(range(0, 4)),
+                         lrb_rank),
                      Arm(f"layers4-23-int4g{int4_group}", 4, int4_group, POLICY_PERSISTENT, rounding,
-                         tuple(range(4, 24)))),
+                         tuple(range(4, 24)), lrb_rank)),
                     shared_inputs=False)
 
 
@@ -199,3 +202,7 @@ WORKLOADS["stack24-dither"] = _stack24_variant(
     "stack24-dither", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-dither", ROUND_DITHER, 32)
 WORKLOADS["stack24-g16"] = _stack24_variant(
     "stack24-g16", "gdn24-512x32-128x128-mixed-int8g64-int4g16-persistent-bdr", ROUND_BDR, 16)
+# ... and with a rank-4 Low-Rank Bypass in every layer
+WORKLOADS["stack24-lrb4"] = _stack24_variant(
+    "stack24-lrb4", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-bdr-lrb4", ROUND_BDR, 32,
+    lrb_rank=4)

@@ -69,4 +69,17 @@ def algorithmic_bytes(cfg: LsqConfig, with_o_ref: bool = False) -> int:
             state += 2 * 4 * dv * dk
     ins = 4 * (2 * dk + dv + (dk if cfg.decay == DECAY_DIAG else 1) + 1)
     outs = 4 * dv * (2 if (with_o_ref and cfg.policy == POLICY_YOKED) else 1)
-    return n * (state + ins + outs)
+    lrb = 0
+    if cfg.lrb_rank > 0:
+        # bypass slots, averaged over a merge period: step j of the period reads
+        # the j filled slots (a [Dv], b [Dk]) and, unless it merges, writes the
+        # new slot and the slots its decay changed (a under scalar decay, b
+        # under diagonal decay)
+        r, diag = cfg.lrb_rank, cfg.decay == DECAY_DIAG
+        tot = 0
+        for j in range(r):
+            tot += j * (dv + dk)
+            if j < r - 1:
+                tot += (dv + dk) + j * (dk if diag else dv)
+        lrb = 4 * tot // r
+    return n * (state + ins + outs + lrb)
