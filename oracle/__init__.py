@@ -79,11 +79,12 @@ def lib():
             L.lsqo_calibrate.argtypes = [cfgp, P, P, P, P, P]
             L.lsqo_step_lrb.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P,
                                         ctypes.POINTER(_Stats), P, P]
+            L.lsqo_prefill.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P]
             L.lsqo_dequantize.argtypes = [cfgp, P, P, P]
             L.lsqo_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
             L.lsqo_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
             for f in (L.lsqo_check_config, L.lsqo_step, L.lsqo_step_trace, L.lsqo_run, L.lsqo_calibrate,
-                      L.lsqo_step_lrb,
+                      L.lsqo_step_lrb, L.lsqo_prefill,
                       L.lsqo_dequantize, L.lsqo_pack, L.lsqo_unpack):
                 f.restype = ctypes.c_int
             _lib = L
@@ -237,6 +238,24 @@ def run(cfg: OracleConfig, st: OracleState, q, k, v, alpha, beta, nthreads: int 
     if rc:
         raise RuntimeError("oracle run failed")
     return o, o_ref
+
+
+def prefill(cfg: OracleConfig, st: OracleState, k, v, alpha, beta, chunk: int = 64) -> None:
+    """Chunkwise prefill of T tokens (inputs with a leading [T] axis) into the
+    quantised state ``st``, in place (linear write, delta = 0)."""
+    _check(cfg)
+    T = int(np.shape(k)[0])
+    n = cfg.n
+    k, v, alpha, beta = map(_f32, (k, v, alpha, beta))
+    ashape = (T, n, cfg.dk) if cfg.decay == DECAY_DIAG else (T, n)
+    for name, a, shp in (("k", k, (T, n, cfg.dk)), ("v", v, (T, n, cfg.dv)),
+                         ("alpha", alpha, ashape), ("beta", beta, (T, n))):
+        if a.shape != shp:
+            raise ValueError(f"oracle: {name} has shape {a.shape}, expected {shp}")
+    rc = lib().lsqo_prefill(ctypes.byref(cfg.c()), T, int(chunk), _p(st.codes), _p(st.scales),
+                            _p(k), _p(v), _p(alpha), _p(beta))
+    if rc:
+        raise RuntimeError("oracle prefill failed")
 
 
 def calibrate(cfg: OracleConfig, S) -> OracleState:

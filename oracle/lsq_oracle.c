@@ -475,6 +475,96 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
   return 0;
 }
 
+/* symmetric INT8 absmax quantisation of a block (the chunk operands) */
+static float quantise_block_i8(const float* x, int64_t n, int8_t* q) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  const float s = amax / 127.0f;
+  const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+  for (int64_t i = 0; i < n; ++i)
+    q[i] = (int8_t)clampd(round_half_even((double)x[i] * (double)inv), -127, 127);
+  return s;
+}
+
+int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes, float* scales,
+                 const float* k, const float* v, const float* alpha, const float* beta) {
+  if (lsqo_check_config(cfg) || cfg->bits == 32 || cfg->delta != 0 || T < 0 || chunk < 1) return -1;
+  if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT) return -1;
+  const int dk = cfg->dk, dv = cfg->dv, g = cfg->group, ng = dk / g, qm = qmax_of(cfg->bits);
+  const int diag = cfg->decay == LSQO_DECAY_DIAG;
+  const int64_t nh = (int64_t)cfg->batch * cfg->heads;
+  const int da = diag ? dk : 1;                 /* decay values per token */
+  float* S = (float*)malloc(sizeof(float) * (size_t)dv * dk);     /* dequantised state */
+  float* G = (float*)malloc(sizeof(float) * (size_t)chunk * da);  /* Gamma-> per token */
+  float* gam = (float*)malloc(sizeof(float) * (size_t)da);        /* gamma^C */
+  float* BV = (float*)malloc(sizeof(float) * (size_t)chunk * dv);
+  float* GK = (float*)malloc(sizeof(float) * (size_t)chunk * dk);
+  int8_t* Vq = (int8_t*)malloc((size_t)chunk * dv);
+  int8_t* Kq = (int8_t*)malloc((size_t)chunk * dk);
+  for (int64_t h = 0; h < nh; ++h) {
+    int8_t* Ch = codes + h * (int64_t)dv * dk;
+    float* sh = scales + h * (int64_t)dv * ng;
+    for (int r = 0; r < dv; ++r)
+      for (int c = 0; c < dk; ++c) S[r * dk + c] = (float)Ch[r * dk + c] * sh[r * ng + c / g];
+    for (int32_t t0 = 0; t0 < T; t0 += chunk) {
+      const int tc = (T - t0 < chunk) ? (int)(T - t0) : chunk;
+      /* decay products: Gamma->_t = prod_{s>t} alpha_s within the chunk */
+      for (int a = 0; a < da; ++a) {
+        float acc = 1.0f;
+        for (int t = tc - 1; t >= 0; --t) {
+          G[t * da + a] = acc;
+          const float* at = alpha + ((int64_t)(t0 + t) * nh + h) * da;
+          acc = acc * at[a];
+        }
+        gam[a] = acc;
+      }
+      /* chunk operands */
+      for (int t = 0; t < tc; ++t) {
+        const int64_t row = (int64_t)(t0 + t) * nh + h;
+        const float b = beta[row];
+        for (int i = 0; i < dv; ++i) BV[t * dv + i] = b * v[row * dv + i];
+        for (int c = 0; c < dk; ++c) GK[t * dk + c] = G[t * da + (diag ? c : 0)] * k[row * dk + c];
+      }
+      const float s_v = quantise_block_i8(BV, (int64_t)tc * dv, Vq);
+      const float s_k = quantise_block_i8(GK, (int64_t)tc * dk, Kq);
+      const float sc = s_v * s_k;
+      /* state pass, row by row */
+      for (int r = 0; r < dv; ++r) {
+        float* x = S + r * dk;
+        for (int c = 0; c < dk; ++c) {
+          int64_t hacc = 0;
+          for (int t = 0; t < tc; ++t) hacc += (int64_t)Vq[t * dv + r] * (int64_t)Kq[t * dk + c];
+          const float H = (float)hacc * sc;
+          x[c] = fmaf(gam[diag ? c : 0], x[c], H);
+        }
+        for (int gi = 0; gi < ng; ++gi) {
+          float snew = sh[r * ng + gi];
+          if (cfg->policy == LSQO_POLICY_DYNAMIC) {
+            float amax = 0.0f;
+            for (int c = gi * g; c < (gi + 1) * g; ++c) {
+              float a = fabsf(x[c]);
+              if (a > amax) amax = a;
+            }
+            snew = amax / (float)qm;
+          }
+          const float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
+          for (int c = gi * g; c < (gi + 1) * g; ++c) {
+            const double q = clampd(round_half_even((double)x[c] * (double)inv), -qm, qm);
+            Ch[r * dk + c] = (int8_t)q;
+            x[c] = (float)q * snew;   /* the dequantised state carried to the next chunk */
+          }
+          sh[r * ng + gi] = snew;
+        }
+      }
+    }
+  }
+  free(S); free(G); free(gam); free(BV); free(GK); free(Vq); free(Kq);
+  return 0;
+}
+
 int lsqo_calibrate(const lsqo_config* cfg, const float* S, int8_t* codes, float* scales,
                    float* ref, float* f32) {
   if (lsqo_check_config(cfg)) return -1;

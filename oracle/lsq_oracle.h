@@ -51,6 +51,19 @@
  *    the buffer is emptied: elements whose code changes are the merged
  *    "sufficiently large" ones, the rest of the buffer is dropped.  Between
  *    merges the state is requantised from S' alone.
+ *  - "LinQuant: Functional Invariances for Low-Precision Linear Recurrences"
+ *    (summary page), Methodology, Low-Precision Chunkwise Realization: the
+ *    state write H_[i] = Q(B_[i] V_[i])^T Q(Gamma->_[i] (.) K_[i]) and the
+ *    state pass S_[i+1] = Q(gamma^C_[i] S_[i] + H_[i]) (lsqo_prefill, the
+ *    linear write delta = 0).  Readings: Gamma->_t is the product of the
+ *    decays of the chunk's later tokens (suffix product in fp32 from the end),
+ *    gamma^C the product of all the chunk's decays; B V = fl(beta_t v_t);
+ *    "Q with implicit scales" on the operands is one symmetric INT8 absmax
+ *    scale per operand block (per head and chunk): s = fl(absmax/127), codes
+ *    clamp(RNE(x fl(1/s))); the integer product is exact, H = fl(h fl(s_V s_K));
+ *    the state pass is X = fma(gamma, S_[i], H) requantised in the state's
+ *    own group format and policy with round-to-nearest-even, and S_[i] is the
+ *    dequantised state fl(C s).
  *
  * State layout used by the oracle (unpacked, host memory, heads = batch*heads):
  *   codes  int8  [heads][Dv][Dk]        signed codes in [-qmax, qmax]
@@ -128,6 +141,14 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
                   float* lrb_b, const float* q, const float* k, const float* v,
                   const float* alpha, const float* beta, float* o, lsqo_stats* stats,
                   double* y_out, double* yp_out);
+
+/* Chunkwise prefill of T tokens into the quantised state (delta = 0; dynamic
+ * or persistent policy; bits 4 or 8): chunks of `chunk` tokens, the last one
+ * possibly shorter.  Inputs k [T][heads][Dk], v [T][heads][Dv], alpha
+ * [T][heads] or [T][heads][Dk], beta [T][heads]; codes and scales updated in
+ * place (scales stay for the persistent policy). */
+int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes, float* scales,
+                 const float* k, const float* v, const float* alpha, const float* beta);
 
 /* Quantise an fp32 state S [heads][Dv][Dk] into this configuration: one scale
  * per group from the group's absolute maximum, codes by round-to-nearest-even

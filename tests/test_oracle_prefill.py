@@ -1,0 +1,118 @@
+"""Pins of the oracle's chunkwise prefill state pass (lsqo_prefill).
+
+The LinQuant summary (Methodology, Low-Precision Chunkwise Realization) writes
+the chunk state as H = Q(B V)^T Q(Gamma-> (.) K) and passes it on with
+S_[i+1] = Q(gamma^C S_[i] + H).  Tied here to things other than its own code:
+  * operands chosen on the INT8 grids: one chunk reproduces the exact sum of
+    v_t k_t^T to within half a state step per element;
+  * the chunk recursion against the token-by-token fp32 recurrence of Eq. (1)
+    (the oracle's unquantised mode, delta = 0), within the error the operand
+    and state quantisers allow, for scalar and diagonal decay, with a short
+    last chunk;
+  * the decay bookkeeping in closed form: a lone token t of a chunk enters H
+    with the product of the later decays, a^(C-1-t) for a constant a, and a
+    chunk without writes multiplies the state by the product of all its decays;
+  * T = 0 changes nothing.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import OracleConfig
+
+
+def _cfg(n=2, dk=64, dv=32, bits=8, group=32, policy=oracle.POLICY_DYNAMIC, decay=0):
+    return OracleConfig(batch=1, heads=n, dk=dk, dv=dv, bits=bits, group=group, policy=policy,
+                        rounding=oracle.ROUND_RNE, delta=0, decay=decay)
+
+
+def test_grid_operands_give_the_exact_sum_within_half_a_step():
+    rng = np.random.default_rng(1)
+    cfg = _cfg()
+    T = 40                                   # one chunk
+    v = rng.integers(-127, 128, (T, 2, 32)) * 2.0 ** -7
+    k = rng.integers(-127, 128, (T, 2, 64)) * 2.0 ** -10
+    v[0, :, 0] = 127 * 2.0 ** -7             # absmax on the grid: scale 2^-7 exactly
+    k[0, :, 0] = 127 * 2.0 ** -10
+    st = oracle.zero_state(cfg)
+    oracle.prefill(cfg, st, k, v, np.ones((T, 2)), np.ones((T, 2)), chunk=64)
+    X = np.einsum("tni,tnj->nij", v, k)      # exact in float64
+    deq = oracle.dequantize(cfg, st)
+    s = np.repeat(st.scales, 32, axis=-1)
+    assert np.all(np.abs(deq - X) <= 0.5 * s * (1 + 1e-6))
+    Xg = np.abs(X).reshape(2, 32, 2, 32).max(-1)
+    assert np.allclose(st.scales, Xg / 127, rtol=1e-6)
+
+
+@pytest.mark.parametrize("decay", [0, 1])
+@pytest.mark.parametrize("T", [64, 100, 192])
+def test_chunks_follow_the_token_recurrence(decay, T):
+    rng = np.random.default_rng(7)
+    n, dk, dv = 2, 64, 32
+    cfg = _cfg(n=n, dk=dk, dv=dv, decay=decay)
+    k = rng.standard_normal((T, n, dk)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, n, dv)).astype(np.float32)
+    if decay:
+        a = rng.uniform(0.95, 1.0, (T, n, dk)).astype(np.float32)
+    else:
+        a = rng.uniform(0.95, 1.0, (T, n)).astype(np.float32)
+    b = rng.uniform(0.3, 1.0, (T, n)).astype(np.float32)
+    st = oracle.zero_state(cfg)
+    oracle.prefill(cfg, st, k, v, a, b, chunk=64)
+    # the unquantised token recurrence (q is irrelevant for the state)
+    fcfg = cfg.replace(bits=32, policy=oracle.POLICY_NONE)
+    fst = oracle.zero_state(fcfg)
+    oracle.run(fcfg, fst, np.zeros_like(k), k, v, a, b)
+    deq = oracle.dequantize(cfg, st)
+    ref = fst.f32
+    err = np.abs(deq - ref).max() / np.abs(ref).max()
+    assert err < 0.03, err                   # INT8 operands and state: a few 1/127 steps
+
+
+def test_a_lone_token_enters_with_the_product_of_later_decays():
+    n, dk, dv, C = 1, 64, 32, 16
+    cfg = _cfg(n=n, dk=dk, dv=dv, policy=oracle.POLICY_PERSISTENT)
+    a = 0.8
+    k1 = np.zeros(dk, np.float32); k1[3] = 1.0
+    v1 = np.zeros(dv, np.float32); v1[5] = 1.0
+    vals = []
+    for t in range(C):
+        k = np.zeros((C, n, dk), np.float32); k[t, 0] = k1
+        v = np.zeros((C, n, dv), np.float32); v[t, 0] = v1
+        st = oracle.zero_state(cfg)
+        st.scales[:] = 2.0 ** -6                # state step 1/64, range +-1.98
+        oracle.prefill(cfg, st, k, v, np.full((C, n), a, np.float32), np.ones((C, n), np.float32),
+                       chunk=C)
+        vals.append(float(oracle.dequantize(cfg, st)[0, 5, 3]))
+    # the operand quantiser maps a lone token's block to 127 exactly: H = a^(C-1-t)
+    want = [a ** (C - 1 - t) for t in range(C)]
+    assert np.allclose(vals, want, rtol=0, atol=2.0 ** -7)   # half a state step
+
+
+def test_a_chunk_without_writes_decays_the_state():
+    rng = np.random.default_rng(3)
+    n, dk, dv, C = 2, 64, 16, 32
+    cfg = _cfg(n=n, dk=dk, dv=dv, policy=oracle.POLICY_PERSISTENT, group=64)
+    S = rng.standard_normal((n, dv, dk)).astype(np.float32)
+    st = oracle.calibrate(cfg, S)
+    c0 = st.codes.astype(np.float64)
+    a = rng.uniform(0.9, 1.0, (C, n)).astype(np.float32)
+    z = np.zeros((C, n, dk), np.float32)
+    oracle.prefill(cfg, st, z, np.zeros((C, n, dv), np.float32), a, np.ones((C, n), np.float32),
+                   chunk=C)
+    gam = np.ones(n, np.float32)
+    for t in range(C - 1, -1, -1):           # the chunk's product of decays, in fp32
+        gam = (gam * a[t]).astype(np.float32)
+    want = np.clip(np.round(c0 * gam[:, None, None].astype(np.float64)), -127, 127)
+    near = np.abs(np.abs(c0 * gam[:, None, None] - np.floor(c0 * gam[:, None, None])) - 0.5) < 1e-5
+    assert np.array_equal(st.codes[~near], want[~near])
+
+
+def test_empty_prompt_changes_nothing():
+    cfg = _cfg()
+    st = oracle.calibrate(cfg, np.random.default_rng(0).standard_normal((2, 32, 64)).astype(np.float32))
+    before = st.copy()
+    oracle.prefill(cfg, st, np.zeros((0, 2, 64)), np.zeros((0, 2, 32)), np.zeros((0, 2)),
+                   np.zeros((0, 2)))
+    assert np.array_equal(st.codes, before.codes) and np.array_equal(st.scales, before.scales)
