@@ -202,6 +202,32 @@ lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float*
                           const float* v, const float* alpha, const float* beta, float* o,
                           float* o_ref, void* stream);
 
+/* Chunkwise prefill of T tokens (linear write, no readout), after the
+ * low-precision chunkwise realisation in the Methodology of "LinQuant:
+ * Functional Invariances for Low-Precision Linear Recurrences".  Tokens are
+ * taken in chunks of 64 (the last one may be shorter).  Per chunk and head:
+ *   Gamma->_t  product of the decays of the chunk's later tokens (fp32, from
+ *              the chunk's end; the diagonal decay per column),
+ *   gamma^C    the product over the whole chunk,
+ *   H          = Q(beta v)^T Q(Gamma-> (.) k): each operand block ([tokens x
+ *              Dv] and [tokens x Dk]) is quantised to INT8 with one absmax
+ *              scale s = max|x| / 127 and round-half-even codes; the integer
+ *              product is exact and H = fl(h * fl(s_V * s_K)),
+ *   X          = fma(gamma^C, S, H), requantised in the state's own group
+ *              format and policy with round-half-even; the dequantised state
+ *              fl(code * s) is carried to the next chunk.
+ * Inputs carry a leading [T] axis (contiguous, token-major): k [T][heads][Dk],
+ * v [T][heads][Dv], alpha [T][heads] (or [T][heads][Dk] for a diagonal
+ * decay), beta [T][heads]; device pointers, 4-byte aligned, read-only.
+ * Supported: bits 4 and 8; policy DYNAMIC or PERSISTENT (calibrated first);
+ * delta 0 (the delta-rule write is sequential per token: use
+ * lsq_decode_run); no bypass (lrb_rank 0); Dk and Dv in {64, 128};
+ * otherwise UNSUPPORTED.  The state pass rounds half to even whatever the
+ * handle's rounding field says.  T = 0 or no heads: nothing to do.  The step
+ * index advances by T.  One workgroup per head walks the chunks in order. */
+lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
+                       const float* alpha, const float* beta, void* stream);
+
 /* Static description of a status code. */
 const char* lsq_status_string(lsq_status s);
 

@@ -21,7 +21,7 @@ DECAY_SCALAR, DECAY_DIAG = 0, 1
 __all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_alloc",
            "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_set_calibrated",
            "lsq_state_step_index", "lsq_state_set_step_index",
-           "lsq_decode_step", "lsq_decode_run", "lsq_status_string", "lsq_version"]
+           "lsq_decode_step", "lsq_decode_run", "lsq_prefill", "lsq_status_string", "lsq_version"]
 
 
 @dataclass(frozen=True)
@@ -118,6 +118,12 @@ def lsq_decode_run(handle: int, H: int, q, k, v, alpha, beta, o, o_ref=None, str
     _lib.check(_lib.load().lsq_decode_run(handle, int(H), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                           _ptr(beta), _ptr(o), _ptr(o_ref), _stream_ptr(stream)),
                "lsq_decode_run")
+
+
+def lsq_prefill(handle: int, T: int, k, v, alpha, beta, stream=None) -> None:
+    _lib.check(_lib.load().lsq_prefill(handle, int(T), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _stream_ptr(stream)),
+               "lsq_prefill")
 
 
 def lsq_status_string(status: int) -> str:
@@ -231,6 +237,17 @@ class LsqState:
             o_ref = self._out(None, (H,))
         lsq_decode_run(self.handle, H, q, k, v, alpha, beta, o, o_ref, stream)
         return (o, o_ref) if self.cfg.policy == POLICY_YOKED else o
+
+    def prefill(self, k, v, alpha, beta, stream=None):
+        """Chunkwise prefill over T tokens (inputs with a leading [T] axis, no q)."""
+        c = self.cfg
+        T = int(k.shape[0])
+        _check_tensor("k", k, (T, c.n, c.dk))
+        _check_tensor("v", v, (T, c.n, c.dv))
+        _check_tensor("alpha", alpha, (T,) + ((c.n, c.dk) if c.decay == DECAY_DIAG else (c.n,)))
+        _check_tensor("beta", beta, (T, c.n))
+        lsq_prefill(self.handle, T, k, v, alpha, beta, stream)
+        return self
 
 
 def _check_tensor(name, t, shape):

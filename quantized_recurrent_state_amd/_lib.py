@@ -65,6 +65,7 @@ def load() -> ctypes.CDLL:
         "lsq_state_set_step_index": [P, ctypes.c_int64],
         "lsq_decode_step": [P, P, P, P, P, P, P, P, P],
         "lsq_decode_run": [P, ctypes.c_int32, P, P, P, P, P, P, P, P],
+        "lsq_prefill": [P, ctypes.c_int32, P, P, P, P, P],
         "lsq_status_string": [ctypes.c_int],
         "lsq_last_error": [],
         "lsq_version": [],

@@ -347,6 +347,47 @@ lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float*
   return ok();
 }
 
+lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
+                       const float* alpha, const float* beta, void* stream) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  if (T < 0) return fail(LSQ_ERR_INVALID_ARG, "negative token count");
+  const lsq_config& c = st->cfg;
+  if (c.bits != 4 && c.bits != 8) return fail(LSQ_ERR_UNSUPPORTED, "prefill needs a quantised state");
+  if (c.policy != LSQ_POLICY_DYNAMIC && c.policy != LSQ_POLICY_PERSISTENT)
+    return fail(LSQ_ERR_UNSUPPORTED, "prefill supports the DYNAMIC and PERSISTENT policies");
+  if (c.delta != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill supports the linear write (delta 0)");
+  if (c.lrb_rank != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill does not take the bypass");
+  if (c.dv != 64 && c.dv != 128)
+    return fail(LSQ_ERR_UNSUPPORTED, "dv %d: prefill has dv 64 and 128", c.dv);
+  if (c.dk / c.group > 8) return fail(LSQ_ERR_UNSUPPORTED, "prefill holds at most 8 groups per row");
+  if (c.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
+    return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");
+  if (T == 0 || n_heads(c) == 0) {
+    st->step += T;
+    return ok();
+  }
+  if (!k || !v || !alpha || !beta) return fail(LSQ_ERR_INVALID_ARG, "k, v, alpha and beta must be non-null");
+  if (!aligned4(k) || !aligned4(v) || !aligned4(alpha) || !aligned4(beta))
+    return fail(LSQ_ERR_INVALID_ARG, "k, v, alpha and beta must be 4-byte aligned");
+  if (n_heads(c) > INT32_MAX) return fail(LSQ_ERR_UNSUPPORTED, "too many heads for one launch");
+  lsq::PrefillArgs a{};
+  a.codes = static_cast<uint8_t*>(st->codes);
+  a.scales = st->scales;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.n_heads = (int32_t)n_heads(c);
+  a.T = T;
+  a.ng = c.dk / c.group;
+  a.group = c.group;
+  hipError_t e = lsq::launch_prefill(a, c.bits, c.dk, c.dv, c.policy,
+                                     c.decay == LSQ_DECAY_DIAG, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "prefill launch");
+  st->step += T;
+  return ok();
+}
+
 const char* lsq_status_string(lsq_status s) {
   switch (s) {
     case LSQ_OK: return "LSQ_OK";
@@ -361,6 +402,6 @@ const char* lsq_status_string(lsq_status s) {
 
 const char* lsq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t lsq_version(void) { return 101; }
+int32_t lsq_version(void) { return 102; }
 
 }  // extern "C"

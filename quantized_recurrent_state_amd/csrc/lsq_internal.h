@@ -50,6 +50,18 @@ struct CalibArgs {
   int32_t nit, waves_per_head, total_waves;
 };
 
+// Arguments of a chunkwise prefill launch (linear write): the handle's packed
+// state is advanced over T tokens, one workgroup per head.
+struct PrefillArgs {
+  uint8_t* codes;        // [n][dv][dk*bits/8]
+  float* scales;         // [n][dv][ng]
+  const float* k;        // [T][n][dk]
+  const float* v;        // [T][n][dv]
+  const float* alpha;    // [T][n] or [T][n][dk]
+  const float* beta;     // [T][n]
+  int32_t n_heads, T, ng, group;
+};
+
 // Launch geometry shared by the host and the kernels.
 struct Geometry {
   int32_t lanes_per_row;   // lanes covering one state row
@@ -68,6 +80,8 @@ hipError_t launch_step_f32(const StepArgs& a, int dk, int delta, int diag, hipSt
 hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s);
 hipError_t launch_lrb_step(const StepArgs& a, int bits, int dk, int policy, int rounding,
                            int delta, int diag, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int bits, int dk, int dv, int policy, int diag,
+                          hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace lsq

@@ -206,3 +206,32 @@ WORKLOADS["stack24-g16"] = _stack24_variant(
 WORKLOADS["stack24-lrb4"] = _stack24_variant(
     "stack24-lrb4", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-bdr-lrb4", ROUND_BDR, 32,
     lrb_rank=4)
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    """A synthetic chunkwise-prefill workload: T prompt tokens into every head's state."""
+    name: str
+    recipe: str
+    batch: int
+    heads: int
+    dk: int
+    dv: int
+    decay: int
+    tokens: int
+    bits: int
+    group: int
+    policy: int
+
+    def config(self) -> dict:
+        return dict(batch=self.batch, heads=self.heads, dk=self.dk, dv=self.dv, bits=self.bits,
+                    group=self.group, policy=self.policy, rounding=ROUND_RNE, delta=0,
+                    decay=self.decay)
+
+
+PREFILL_WORKLOADS = {
+    # GLA-style diagonal decay (the linear write the chunkwise form covers): a 4096-token
+    # prompt into batch 64 x 16 heads of INT4 g32 state, dynamic scale from S_0 = 0
+    "prefill-gla": PrefillWorkload("gla-prefill-64x16-128x128-int4g32-dynamic-T4096", "gla", 64, 16,
+                                   128, 128, DECAY_DIAG, 4096, 4, 32, POLICY_DYNAMIC),
+}

@@ -141,3 +141,51 @@ def test_step_index_is_host_state():
     assert L.lsq_decode_run(h, 3, None, None, None, None, None, None, None, None) == 0
     assert lsq.lsq_state_step_index(h) == 4
     lsq.lsq_state_free(h)
+
+
+def _alloc_all(cfg):
+    """A handle whose every needed buffer is the untouched FAKE address."""
+    L = _lib.load()
+    need = lsq.lsq_state_sizes(cfg)
+    p = [FAKE if n else None for n in need]
+    bufs = _lib.lsq_buffers(p[0], need[0], p[1], need[1], p[2], need[2], p[3], need[3],
+                            p[4], need[4])
+    h = ctypes.c_void_p()
+    assert L.lsq_state_alloc(ctypes.byref(cfg.c()), ctypes.byref(bufs), ctypes.byref(h)) == 0
+    return h.value
+
+
+@pytest.mark.parametrize("change", [
+    dict(delta=1), dict(policy=lsq.POLICY_YOKED), dict(bits=32, group=1, policy=lsq.POLICY_NONE),
+    dict(dv=32), dict(dv=256), dict(lrb_rank=2),
+])
+def test_prefill_rejects_unsupported_handles(change):
+    base = dict(batch=1, heads=2, dk=128, dv=128, bits=4, group=32, policy=lsq.POLICY_DYNAMIC)
+    base.update(change)
+    cfg = lsq.LsqConfig(**base)
+    h = _alloc_all(cfg)
+    st = _lib.load().lsq_prefill(h, 64, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == 2, _lib.load().lsq_last_error()
+    lsq.lsq_state_free(h)
+
+
+def test_prefill_argument_checks_before_launch():
+    L = _lib.load()
+    cfg = lsq.LsqConfig(1, 2, 128, 64, 8, 16, lsq.POLICY_PERSISTENT)
+    h = _alloc_all(cfg)
+    p = [FAKE] * 4
+    assert L.lsq_prefill(h, 64, *p, None) == 4                 # persistent, not calibrated
+    assert L.lsq_state_set_calibrated(h, 1) == 0
+    assert L.lsq_prefill(h, -1, *p, None) == 1                 # negative T
+    assert L.lsq_prefill(h, 64, None, *p[1:], None) == 1       # null input
+    assert L.lsq_prefill(h, 64, FAKE + 2, *p[1:], None) == 1   # misaligned input
+    assert L.lsq_prefill(None, 64, *p, None) == 1
+    assert lsq.lsq_state_step_index(h) == 0
+    assert L.lsq_prefill(h, 0, *p, None) == 0                  # no tokens: nothing to do
+    lsq.lsq_state_free(h)
+    # an empty batch only advances the sequence position
+    cfg0 = lsq.LsqConfig(0, 4, 128, 128, 4, 32, lsq.POLICY_DYNAMIC)
+    st, h = _alloc(cfg0, codes=None, scales=None)
+    assert L.lsq_prefill(h, 100, None, None, None, None, None) == 0
+    assert lsq.lsq_state_step_index(h) == 100
+    lsq.lsq_state_free(h)
