@@ -45,76 +45,104 @@ __device__ __forceinline__ int rne_code(float x, float inv, float qmax) {
 template <int BITS, int DK, int DV, int POLICY, int DIAG>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
-  constexpr int TR = DV / 64;            // tile rows per wave
-  constexpr int TC = DK / 16;            // tile columns
-  constexpr int ROWB = DK * BITS / 8;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int RT = DV / 64;            // 16-row tiles per wave
+  constexpr int CT = DK / 16;            // 16-column tiles
+  constexpr int ROWB = DK * BITS / 8;    // packed bytes per state row
+  constexpr int SP = DK + 8;             // LDS pitch of a state code row (bank spread)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x;
   const int ng = a.ng, g = a.group;
 
   __shared__ __align__(16) int8_t vt[DV * kOpRow];      // (B V)^T codes [dv][token]
   __shared__ __align__(16) int8_t kt[DK * kOpRow];      // (Gamma-> K)^T codes [dk][token]
-  __shared__ __align__(16) int8_t stage[DV * DK];       // state codes [dv][dk]
+  __shared__ __align__(16) int8_t stage[DV * SP];       // state codes [dv][dk]
   __shared__ float sscale[DV * 8];                      // state scales [dv][ng] (ng <= 8)
-  __shared__ float gam[DK];                             // gamma^C per column
+  __shared__ __align__(16) float gam[DK];               // gamma^C per column
   __shared__ unsigned amax_bits[2];                     // operand block maxima (V, K)
 
+  // ---- the head's packed state -> LDS codes and scales.  The state stays
+  // there as codes between chunks: the carried value is fl(code * scale).
   const size_t hrow0 = (size_t)h * DV;
-  // ---- the head's packed state -> LDS codes and scales
-  for (int idx = tid; idx < DV * DK; idx += 256) {
-    const int r = idx / DK, c = idx % DK;
-    const uint8_t byte = a.codes[(hrow0 + r) * ROWB + (BITS == 4 ? c / 2 : c)];
-    int code;
-    if constexpr (BITS == 4) code = ((int)(((c & 1) ? (byte >> 4) : byte) & 0xF) ^ 8) - 8;
-    else code = (int)(int8_t)byte;
-    stage[idx] = (int8_t)code;
+  const uint32_t* gcodes = reinterpret_cast<const uint32_t*>(a.codes + hrow0 * ROWB);
+  for (int idx = tid; idx < DV * ROWB / 4; idx += 256) {
+    const int r = idx / (ROWB / 4), w = idx % (ROWB / 4);
+    const uint32_t word = gcodes[idx];
+    if constexpr (BITS == 4) {           // 8 nibbles -> 8 sign-extended bytes
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lo |= (uint32_t)((((word >> (4 * q)) & 0xF) ^ 8) - 8) << (8 * q) & (0xFFu << (8 * q));
+        hi |= (uint32_t)((((word >> (4 * q + 16)) & 0xF) ^ 8) - 8) << (8 * q) & (0xFFu << (8 * q));
+      }
+      *reinterpret_cast<uint32_t*>(&stage[r * SP + 8 * w]) = lo;
+      *reinterpret_cast<uint32_t*>(&stage[r * SP + 8 * w + 4]) = hi;
+    } else {
+      *reinterpret_cast<uint32_t*>(&stage[r * SP + 4 * w]) = word;
+    }
   }
   for (int idx = tid; idx < DV * ng; idx += 256) sscale[idx] = a.scales[hrow0 * ng + idx];
   __syncthreads();
-  // dequantised state in the accumulator layout: S[I][J][v]
-  float S[TR][TC][4];
-#pragma unroll
-  for (int I = 0; I < TR; ++I)
-#pragma unroll
-    for (int J = 0; J < TC; ++J)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 16 * (wave * TR + I) + 4 * (lane / 16) + v, c = 16 * J + (lane % 16);
-        S[I][J][v] = (float)stage[r * DK + c] * sscale[r * ng + c / g];
-      }
 
   const int64_t nh = a.n_heads;
+  // Operand roles (wave-uniform): waves covering threads c < Dk own column c
+  // of Gamma-> (.) K, waves covering threads 128 + i own column i of B V.  A
+  // thread's raw inputs for one chunk are p0[t] (k or v) and p1[t] (its decay,
+  // or beta), loaded one chunk ahead so that the next chunk's reads are in
+  // flight during this chunk's product and state pass.
+  const bool krole = wave * 64 < DK, vrole = wave >= 2 && (wave - 2) * 64 < DV;
+  const unsigned ut = threadIdx.x;       // unsigned lane offset: scalar base + vector offset loads
+  float p0[kChunk], p1[kChunk];
+  auto load_chunk = [&](int c0) {
+    const int last_t = min(kChunk, a.T - c0) - 1;   // a short chunk re-reads its last token
+    if (krole) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        const int64_t row = (int64_t)(c0 + min(t, last_t)) * nh + h;
+        const float* kr = a.k + row * DK;           // uniform row base, lane offset
+        p0[t] = kr[ut];
+        if constexpr (DIAG) {
+          const float* ar = a.alpha + row * DK;
+          p1[t] = ar[ut];
+        } else {
+          p1[t] = a.alpha[row];
+        }
+      }
+    } else if (vrole) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        const int64_t row = (int64_t)(c0 + min(t, last_t)) * nh + h;
+        const float* vr = a.v + row * DV;
+        p0[t] = vr[ut - 128u];
+        p1[t] = a.beta[row];
+      }
+    }
+  };
+  if (a.T > 0) load_chunk(0);
+
   for (int t0 = 0; t0 < a.T; t0 += kChunk) {
     const int tc = min(kChunk, a.T - t0);
     // ---- operands: one column per thread, the chunk's tokens in registers
     float col[kChunk];
     float cmax = 0.f;
-    const bool krole = tid < DK, vrole = tid >= 128 && tid < 128 + DV;
     if (krole) {
       float acc = 1.f;                   // Gamma->: product of the later tokens' decays
 #pragma unroll
       for (int t = kChunk - 1; t >= 0; --t) {
-        col[t] = 0.f;
-        if (t < tc) {
-          const int64_t row = (int64_t)(t0 + t) * nh + h;
-          col[t] = acc * a.k[row * DK + tid];
-          acc = acc * (DIAG ? a.alpha[row * DK + tid] : a.alpha[row]);
-        }
+        const bool in = t < tc;
+        col[t] = in ? acc * p0[t] : 0.f;
+        acc = in ? acc * p1[t] : acc;
         cmax = fmaxf(cmax, fabsf(col[t]));
       }
       gam[tid] = acc;
     } else if (vrole) {
-      const int i = tid - 128;
 #pragma unroll
       for (int t = 0; t < kChunk; ++t) {
-        col[t] = 0.f;
-        if (t < tc) {
-          const int64_t row = (int64_t)(t0 + t) * nh + h;
-          col[t] = a.beta[row] * a.v[row * DV + i];
-        }
+        col[t] = t < tc ? p1[t] * p0[t] : 0.f;
         cmax = fmaxf(cmax, fabsf(col[t]));
       }
     }
+    if (t0 + kChunk < a.T) load_chunk(t0 + kChunk);
     if (tid < 2) amax_bits[tid] = 0u;
     __syncthreads();
     if (krole) atomicMax(&amax_bits[1], __float_as_uint(cmax));
@@ -134,89 +162,115 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
     __syncthreads();
-    // ---- H = (B V)^T (Gamma-> K) on the matrix cores
-    i32x4 acc[TR][TC];
+    // ---- H on the matrix cores: A = (Gamma-> K) codes (rows = state columns),
+    // B = (B V) codes (columns = state rows), so that lane l receives
+    // H[16(wave RT + J) + l%16][16 I + 4(l/16) + v], v = 0..3: four adjacent
+    // columns of one state row per tile
+    i32x4 acc[RT][CT];
 #pragma unroll
-    for (int I = 0; I < TR; ++I)
+    for (int J = 0; J < RT; ++J)
 #pragma unroll
-      for (int J = 0; J < TC; ++J) acc[I][J] = i32x4{0, 0, 0, 0};
+      for (int I = 0; I < CT; ++I) acc[J][I] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < kChunk / 32; ++ks) {
       const int koff = 32 * ks + 8 * (lane / 16);
-      long bop[TC];
+      long bv[RT];
 #pragma unroll
-      for (int J = 0; J < TC; ++J)
-        bop[J] = *reinterpret_cast<const long*>(&kt[(16 * J + lane % 16) * kOpRow + koff]);
+      for (int J = 0; J < RT; ++J)
+        bv[J] = *reinterpret_cast<const long*>(&vt[(16 * (wave * RT + J) + lane % 16) * kOpRow + koff]);
 #pragma unroll
-      for (int I = 0; I < TR; ++I) {
-        const long aop =
-            *reinterpret_cast<const long*>(&vt[(16 * (wave * TR + I) + lane % 16) * kOpRow + koff]);
+      for (int I = 0; I < CT; ++I) {
+        const long ak = *reinterpret_cast<const long*>(&kt[(16 * I + lane % 16) * kOpRow + koff]);
 #pragma unroll
-        for (int J = 0; J < TC; ++J)
-          acc[I][J] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[J], acc[I][J], 0, 0, 0);
+        for (int J = 0; J < RT; ++J)
+          acc[J][I] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ak, bv[J], acc[J][I], 0, 0, 0);
       }
     }
     // ---- state pass: X = fma(gamma, S, H), requantised per group
     const float sc = s_v * s_k;
-    const bool last = t0 + kChunk >= a.T;
+    const int tpg = g / 16;              // tiles per group (an aligned power of two)
+    float gc[CT][4];
 #pragma unroll
-    for (int I = 0; I < TR; ++I)
+    for (int I = 0; I < CT; ++I) {
+      if constexpr (DIAG) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&gam[16 * I + 4 * (lane / 16)]);
+        gc[I][0] = q4.x; gc[I][1] = q4.y; gc[I][2] = q4.z; gc[I][3] = q4.w;
+      } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 16 * (wave * TR + I) + 4 * (lane / 16) + v;
-        float x[TC];
+        for (int v = 0; v < 4; ++v) gc[I][v] = gam[0];
+      }
+    }
 #pragma unroll
-        for (int J = 0; J < TC; ++J) {
-          const int c = 16 * J + lane % 16;
-          const float H = (float)acc[I][J][v] * sc;
-          x[J] = fmaf(gam[DIAG ? c : 0], S[I][J][v], H);
-        }
-        // groups of g columns: g/16 tiles (an aligned power of two) x the 16
-        // lanes of a DPP row; butterflies over tiles keep every index static
-        const int tpg = g / 16;
-        float s[TC];
-        if constexpr (POLICY == POL_DYNAMIC) {
-          float m[TC];
+    for (int J = 0; J < RT; ++J) {
+      const int r = 16 * (wave * RT + J) + lane % 16;
+      int8_t* crow = &stage[r * SP + 4 * (lane / 16)];
+      float x[CT][4], s[CT];
 #pragma unroll
-          for (int J = 0; J < TC; ++J) m[J] = fabsf(x[J]);
+      for (int I = 0; I < CT; ++I) {
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(&crow[16 * I]);
+        s[I] = sscale[r * ng + (16 * I) / g];
 #pragma unroll
-          for (int step = 1; step < TC; step *= 2) {
-            if (step < tpg) {
-              float n2[TC];
-#pragma unroll
-              for (int J = 0; J < TC; ++J) n2[J] = fmaxf(m[J], m[J ^ step]);
-#pragma unroll
-              for (int J = 0; J < TC; ++J) m[J] = n2[J];
-            }
-          }
-#pragma unroll
-          for (int J = 0; J < TC; ++J) {
-            s[J] = group_max(m[J], 16) / QMAX;
-            if (lane % 16 == 0 && (J % tpg) == 0) sscale[r * ng + (16 * J) / g] = s[J];
-          }
-        } else {
-#pragma unroll
-          for (int J = 0; J < TC; ++J) s[J] = sscale[r * ng + (16 * J) / g];
-        }
-#pragma unroll
-        for (int J = 0; J < TC; ++J) {
-          const int code = rne_code(x[J], inv_scale(s[J]), QMAX);
-          S[I][J][v] = (float)code * s[J];
-          if (last) stage[r * DK + 16 * J + lane % 16] = (int8_t)code;
+        for (int v = 0; v < 4; ++v) {
+          const float S = (float)(int)(int8_t)(cw >> (8 * v)) * s[I];
+          x[I][v] = fmaf(gc[I][v], S, (float)acc[J][I][v] * sc);
         }
       }
+      if constexpr (POLICY == POL_DYNAMIC) {
+        // group absmax: the tile's four columns in the lane, the group's
+        // tiles by butterflies (static indices), then the four lanes that
+        // hold the row (l%16 fixed)
+        float m[CT];
+#pragma unroll
+        for (int I = 0; I < CT; ++I)
+          m[I] = fmaxf(fmaxf(fabsf(x[I][0]), fabsf(x[I][1])), fmaxf(fabsf(x[I][2]), fabsf(x[I][3])));
+#pragma unroll
+        for (int step = 1; step < CT; step *= 2) {
+          if (step < tpg) {
+            float n2[CT];
+#pragma unroll
+            for (int I = 0; I < CT; ++I) n2[I] = fmaxf(m[I], m[I ^ step]);
+#pragma unroll
+            for (int I = 0; I < CT; ++I) m[I] = n2[I];
+          }
+        }
+#pragma unroll
+        for (int I = 0; I < CT; ++I) {
+          m[I] = fmaxf(m[I], __shfl_xor(m[I], 16));
+          m[I] = fmaxf(m[I], __shfl_xor(m[I], 32));
+          s[I] = m[I] / QMAX;
+          if (lane < 16 && (I % tpg) == 0) sscale[r * ng + (16 * I) / g] = s[I];
+        }
+      }
+#pragma unroll
+      for (int I = 0; I < CT; ++I) {
+        const float inv = inv_scale(s[I]);
+        uint32_t nw = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) nw |= (uint32_t)(rne_code(x[I][v], inv, QMAX) & 0xFF) << (8 * v);
+        *reinterpret_cast<uint32_t*>(&crow[16 * I]) = nw;
+      }
+    }
     __syncthreads();
   }
   if (a.T <= 0) return;
   // ---- LDS codes and scales -> the head's packed state
-  for (int idx = tid; idx < DV * ROWB; idx += 256) {
-    const int r = idx / ROWB, b = idx % ROWB;
-    uint8_t byte;
-    if constexpr (BITS == 4)
-      byte = (uint8_t)((stage[r * DK + 2 * b] & 0xF) | ((stage[r * DK + 2 * b + 1] & 0xF) << 4));
-    else
-      byte = (uint8_t)stage[r * DK + b];
-    a.codes[(hrow0 + r) * ROWB + b] = byte;
+  uint32_t* ocodes = reinterpret_cast<uint32_t*>(a.codes + hrow0 * ROWB);
+  for (int idx = tid; idx < DV * ROWB / 4; idx += 256) {
+    const int r = idx / (ROWB / 4), w = idx % (ROWB / 4);
+    uint32_t word;
+    if constexpr (BITS == 4) {           // 8 bytes -> 8 nibbles
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(&stage[r * SP + 8 * w]);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(&stage[r * SP + 8 * w + 4]);
+      word = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        word |= ((lo >> (8 * q)) & 0xF) << (4 * q);
+        word |= ((hi >> (8 * q)) & 0xF) << (4 * q + 16);
+      }
+    } else {
+      word = *reinterpret_cast<const uint32_t*>(&stage[r * SP + 4 * w]);
+    }
+    ocodes[idx] = word;
   }
   if constexpr (POLICY == POL_DYNAMIC) {
     for (int idx = tid; idx < DV * ng; idx += 256) a.scales[hrow0 * ng + idx] = sscale[idx];
