@@ -17,6 +17,11 @@ roofline    the dominant kernel (the INT4 g32 segment): its algorithmic bytes
             reported only while the kernel sources match the profiled ones
 cpu_baseline  the CPU oracle on a bounded sample of the same workload (sampled
             heads, a few steps, the host threads stated), in the same unit
+
+--workload prefill-gla times the chunkwise prefill instead: a step is one
+4096-token prompt into batch 64 x 16 heads of INT4 g32 state (diagonal decay),
+value = its input and state bytes / wall time; the roofline is the prefill
+kernel's, with its integer matrix-core rate reported beside it.
 """
 from __future__ import annotations
 
@@ -75,10 +80,12 @@ def main() -> int:
     import torch
     import quantized_recurrent_state_amd as lsq
     from quantized_recurrent_state_amd import runner
-    from quantized_recurrent_state_amd.inputs import WORKLOADS
+    from quantized_recurrent_state_amd.inputs import PREFILL_WORKLOADS, WORKLOADS
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in PREFILL_WORKLOADS:
+        return bench_prefill(args, PREFILL_WORKLOADS[args.workload], dev)
     wl = WORKLOADS[args.workload]
     K, W = args.steps, args.warmup
     stream = torch.cuda.current_stream()
@@ -216,6 +223,151 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+PREFILL_SOURCES = ("quantized_recurrent_state_amd/csrc/lsq_prefill.hip",
+                   "quantized_recurrent_state_amd/csrc/lsq_step_impl.h")
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA
+
+
+def bench_prefill(args, wl, dev) -> int:
+    """Chunkwise prefill: a "step" is one prefill of the workload's T-token
+    prompt into every head's state (the state carries over between steps)."""
+    import torch
+    import quantized_recurrent_state_amd as lsq
+    from quantized_recurrent_state_amd import runner
+    from quantized_recurrent_state_amd.inputs import gen_steps
+
+    K, W = args.steps, args.warmup
+    stream = torch.cuda.current_stream()
+    cfg = lsq.LsqConfig(**wl.config())
+    st = lsq.LsqState(cfg, device=dev).zero()
+    t_setup = time.perf_counter()
+    d = gen_steps(wl.recipe, cfg.n, cfg.dk, cfg.dv, [0], 0, wl.tokens, device=dev)
+    inp = [d[x] for x in ("k", "v", "alpha", "beta")]
+    del d
+    torch.cuda.synchronize()
+    log(f"prefill {cfg} T={wl.tokens}: set-up {time.perf_counter() - t_setup:.1f} s")
+    nbytes = runner.prefill_algorithmic_bytes(cfg, wl.tokens)
+    ops = runner.prefill_int8_ops(cfg, wl.tokens)
+
+    def launch():
+        lsq.lsq_prefill(st.handle, wl.tokens, *inp, stream)
+
+    for _ in range(W):
+        launch()
+    torch.cuda.synchronize()
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(K):
+        ev_s[j].record(stream)
+        launch()
+        ev_e[j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]
+    kms = sum(kern_ms) / len(kern_ms)
+    gbs = nbytes * K / wall / 1e9
+    kgbs = nbytes / (kms * 1e-3) / 1e9
+    log(f"timed {K} prefills: {wall * 1e3 / K:.3f} ms each, {gbs:.1f} GB/s; kernel {kms * 1e3:.1f} us")
+
+    h = hashlib.sha256()
+    for rel in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic_prefill.json")
+    if os.path.exists(tf):
+        tr = json.load(open(tf))
+        if tr.get("source_sha") == sha and tr.get("workload") == wl.name:
+            traffic = int(tr["hbm_bytes_per_launch"])
+
+    if args.copy_probe_gib > 0:          # counter calibration, outside the timed region
+        nb = int(args.copy_probe_gib * (1 << 30)) // 256 * 256
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: one device copy of {nb} bytes (read {nb}, written {nb})")
+        del src, dst
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline_prefill(wl, cfg, st, inp, args.cpu_seconds, nbytes)
+
+    line = {
+        "metric": "prefill HBM GB/s of inputs and state (% of peak) and tokens/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8 products, f32 state pass", "data": "synthetic",
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(cfg.n * wl.tokens * K / wall, 1),
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "dk": wl.dk,
+                   "dv": wl.dv, "tokens": wl.tokens, "chunk": 64, "bits": wl.bits,
+                   "group": wl.group, "policy": wl.policy,
+                   "decay": "diag" if wl.decay else "scalar", "bytes_per_step": nbytes,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "prefill_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "launch_us_mean": round(kms * 1e3, 2),
+                     "launch_us_min": round(min(kern_ms) * 1e3, 2), "source_sha": sha},
+        "mfma": {"int8_ops_per_launch": ops, "achieved_tops": round(ops / (kms * 1e-3) / 1e12, 2),
+                 "peak_tops": PEAK_INT8_TOPS,
+                 "frac": round(ops / (kms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_prefill(wl, cfg, st, inp, seconds: float, nbytes: int):
+    """The CPU oracle's prefill on sampled heads (same inputs and start state as
+    the GPU's last prefill), threads over heads, in the benchmark's unit."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    import torch
+    import oracle
+    from tests.parity import ocfg_of, snapshot
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n = cfg.n
+
+    def sample(m):
+        idx = np.linspace(0, n - 1, m).astype(np.int64)
+        sel = torch.as_tensor(idx, device=st.device)
+        s0 = snapshot(st, heads=sel)
+        xs = [x.index_select(1, sel).cpu().numpy() for x in inp]
+        return s0, xs
+
+    def run(m):
+        s0, xs = sample(m)
+        parts = np.array_split(np.arange(m), threads)
+        jobs = []
+        for p in parts:
+            if len(p) == 0:
+                continue
+            oc = ocfg_of(cfg).replace(batch=len(p), heads=1)
+            s = s0.copy()
+            s.codes, s.scales = s.codes[p].copy(), s.scales[p].copy()
+            jobs.append((oc, s, [x[:, p].copy() for x in xs]))
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(len(jobs)) as ex:
+            list(ex.map(lambda j: oracle.prefill(j[0], j[1], *j[2], chunk=64), jobs))
+        return time.perf_counter() - t0
+
+    dt1 = run(threads)
+    m = int(max(threads, min(n, threads * round(seconds / max(dt1, 1e-3)))))
+    dt = run(m)
+    log(f"cpu oracle prefill: {m} sampled heads x {wl.tokens} tokens in {dt:.1f} s on {threads} threads")
+    return {"value": round(nbytes * m / n / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "tokens_per_s": round(m * wl.tokens / dt, 1),
+            "sample": f"{m} of {n} heads (evenly spaced) x the full {wl.tokens}-token prompt, "
+                      f"from the GPU's state, on the same inputs"}
 
 
 def cpu_baseline(arms, seconds: float, steps_avail: int):

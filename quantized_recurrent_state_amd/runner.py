@@ -83,3 +83,20 @@ def algorithmic_bytes(cfg: LsqConfig, with_o_ref: bool = False) -> int:
                 tot += (dv + dk) + j * (dk if diag else dv)
         lrb = 4 * tot // r
     return n * (state + ins + outs + lrb)
+
+
+def prefill_algorithmic_bytes(cfg: LsqConfig, T: int) -> int:
+    """Bytes one prefill of T tokens must move for this handle (all heads): the
+    inputs k, v, alpha, beta read once, the packed codes read and written, the
+    group scales read (and written by the dynamic policy)."""
+    from . import POLICY_DYNAMIC, DECAY_DIAG
+    n, dk, dv = cfg.n, cfg.dk, cfg.dv
+    ins = 4 * T * (dk + dv + (dk if cfg.decay == DECAY_DIAG else 1) + 1)
+    state = 2 * dv * dk * cfg.bits // 8
+    state += dv * (dk // cfg.group) * 4 * (2 if cfg.policy == POLICY_DYNAMIC else 1)
+    return n * (ins + state)
+
+
+def prefill_int8_ops(cfg: LsqConfig, T: int) -> int:
+    """Integer operations of the chunk products H = V^T K over T tokens (2 per MAC)."""
+    return 2 * cfg.n * T * cfg.dk * cfg.dv
