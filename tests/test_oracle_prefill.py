@@ -12,6 +12,10 @@ S_[i+1] = Q(gamma^C S_[i] + H).  Tied here to things other than its own code:
   * the decay bookkeeping in closed form: a lone token t of a chunk enters H
     with the product of the later decays, a^(C-1-t) for a constant a, and a
     chunk without writes multiplies the state by the product of all its decays;
+  * the recursion's Q(.) at every chunk boundary: writes below half a state
+    step vanish across chunks but add up inside one;
+  * INT8 operand codes round half to even (exact ties exposed through the
+    dynamic state scale);
   * T = 0 changes nothing.
 """
 import numpy as np
@@ -116,3 +120,46 @@ def test_empty_prompt_changes_nothing():
     oracle.prefill(cfg, st, np.zeros((0, 2, 64)), np.zeros((0, 2, 32)), np.zeros((0, 2)),
                    np.zeros((0, 2)))
     assert np.array_equal(st.codes, before.codes) and np.array_equal(st.scales, before.scales)
+
+
+def test_the_state_is_requantised_at_every_chunk_boundary():
+    """S_[i+1] = Q(gamma^C S_[i] + H): a write worth 0.49 of a state step is
+    rounded away at the end of its chunk, so two such writes in consecutive
+    chunks leave the state at 0, while the same two writes inside one chunk
+    add exactly (integer product) to 0.98 and round to 1."""
+    n, dk, dv, C = 1, 32, 16, 64
+    cfg = _cfg(n=n, dk=dk, dv=dv, policy=oracle.POLICY_PERSISTENT)
+
+    def prefill(tokens):
+        T = 2 * C
+        k = np.zeros((T, n, dk), np.float32)
+        v = np.zeros((T, n, dv), np.float32)
+        for t in tokens:
+            v[t, 0, 0] = 127 * 2.0 ** -7     # s_V = 2^-7, code 127
+            k[t, 0, 0] = 127 * 2.0 ** -8     # s_K = 2^-8, code 127
+        st = oracle.zero_state(cfg)
+        st.scales[:] = 1.0                   # H = 127^2 2^-15 = 0.4922 state steps per write
+        oracle.prefill(cfg, st, k, v, np.ones((T, n), np.float32), np.ones((T, n), np.float32),
+                       chunk=C)
+        return st.codes
+    assert not prefill([0, C]).any()
+    once = prefill([0, 1])
+    assert once[0, 0, 0] == 1 and np.count_nonzero(once) == 1
+
+
+def test_operand_codes_round_half_to_even():
+    """INT8 operand codes at exact ties: 2.5 -> 2 and 3.5 -> 4.  One token with
+    k = 127 2^-7 e_0 gives H[r][0] = c_r 127 2^-14, so the dynamic scale of row r
+    is c_r 2^-14 exactly and exposes the operand code c_r."""
+    n, dk, dv = 1, 32, 16
+    cfg = _cfg(n=n, dk=dk, dv=dv, group=32)
+    k = np.zeros((1, n, dk), np.float32)
+    v = np.zeros((1, n, dv), np.float32)
+    k[0, 0, 0] = 127 * 2.0 ** -7
+    v[0, 0, :3] = np.array([127, 2.5, 3.5]) * 2.0 ** -7
+    st = oracle.zero_state(cfg)
+    oracle.prefill(cfg, st, k, v, np.ones((1, n), np.float32), np.ones((1, n), np.float32))
+    assert st.scales[0, 0, 0] == 127 * 2.0 ** -14
+    assert st.scales[0, 1, 0] == 2 * 2.0 ** -14
+    assert st.scales[0, 2, 0] == 4 * 2.0 ** -14
+    assert np.all(st.codes[0, :3, 0] == 127)
