@@ -32,6 +32,7 @@ _LIB = os.path.join(_HERE, "liblsq_oracle.so")
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
 ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
 DECAY_SCALAR, DECAY_DIAG = 0, 1
+SCALE_F32, SCALE_F16, SCALE_BF16 = 0, 1, 2
 
 GCC_FLAGS = ["-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
              "-Wall", "-Wextra"]
@@ -52,7 +53,7 @@ def build(force: bool = False) -> str:
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "heads", "dk", "dv", "bits", "group", "policy", "rounding", "delta",
-                 "decay", "lrb_rank")] + [("step", ctypes.c_int64)]
+                 "decay", "lrb_rank", "scale_fmt")] + [("step", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
@@ -87,6 +88,8 @@ def lib():
                       L.lsqo_step_lrb, L.lsqo_prefill,
                       L.lsqo_dequantize, L.lsqo_pack, L.lsqo_unpack):
                 f.restype = ctypes.c_int
+            L.lsqo_scale_as_stored.argtypes = [ctypes.c_float, ctypes.c_int32]
+            L.lsqo_scale_as_stored.restype = ctypes.c_float
             _lib = L
         return _lib
 
@@ -105,6 +108,7 @@ class OracleConfig:
     delta: int = 0
     decay: int = DECAY_SCALAR
     lrb_rank: int = 0      # Low-Rank Bypass slots (0: off)
+    scale_fmt: int = 0     # stored scale format: 0 fp32, 1 binary16, 2 bfloat16
     step: int = 0          # sequence position of the (first) step: dithered rounding, bypass slot
 
     @property
@@ -256,6 +260,11 @@ def prefill(cfg: OracleConfig, st: OracleState, k, v, alpha, beta, chunk: int = 
                             _p(k), _p(v), _p(alpha), _p(beta))
     if rc:
         raise RuntimeError("oracle prefill failed")
+
+
+def scale_as_stored(s: float, fmt: int) -> float:
+    """A group scale rounded to its stored format (SCALE_*), as an fp32 value."""
+    return float(np.float32(lib().lsqo_scale_as_stored(float(s), int(fmt))))
 
 
 def calibrate(cfg: OracleConfig, S) -> OracleState:

@@ -8,7 +8,10 @@
  *
  * Readings taken where the pages are silent (all stated in the design notes):
  *  - symmetric codes in [-qmax, qmax], qmax = 2^(bits-1) - 1, no zero point;
- *  - one fp32 scale per contiguous group of `group` elements along Dk;
+ *  - one scale per contiguous group of `group` elements along Dk, stored in
+ *    fp32 or, by the configuration, rounded to nearest-even binary16 or
+ *    bfloat16; every computed scale is rounded to the stored format first and
+ *    the codes are formed with the stored scale;
  *  - the decay is folded into the group scale before dequantisation:
  *      S'[c] = fl(C[c] * fl(s * alpha_c));
  *  - the output is read from the fp32 state after the update and before it
@@ -41,7 +44,7 @@ int lsqo_check_config(const lsqo_config* cfg) {
   if (cfg->batch < 0 || cfg->heads < 0 || cfg->dk <= 0 || cfg->dv <= 0) return -1;
   if (cfg->delta != 0 && cfg->delta != 1) return -1;
   if (cfg->decay != LSQO_DECAY_SCALAR && cfg->decay != LSQO_DECAY_DIAG) return -1;
-  if (cfg->bits == 32) return cfg->policy == LSQO_POLICY_NONE ? 0 : -1;
+  if (cfg->bits == 32) return (cfg->policy == LSQO_POLICY_NONE && cfg->scale_fmt == 0) ? 0 : -1;
   if (cfg->bits != 4 && cfg->bits != 8) return -1;
   if (cfg->group <= 0 || cfg->dk % cfg->group != 0) return -1;
   if (cfg->bits == 4 && cfg->dk % 2 != 0) return -1;
@@ -52,6 +55,9 @@ int lsqo_check_config(const lsqo_config* cfg) {
       cfg->rounding != LSQO_ROUND_DITHER)
     return -1;
   if (cfg->lrb_rank < 0) return -1;
+  if (cfg->scale_fmt != LSQO_SCALE_F32 && cfg->scale_fmt != LSQO_SCALE_F16 &&
+      cfg->scale_fmt != LSQO_SCALE_BF16)
+    return -1;
   return 0;
 }
 
@@ -69,6 +75,38 @@ static double round_half_even(double y) {
 
 /* Weyl dither of element (r, c) of a head at sequence position `step`:
  * frac(i * 0.618...) in 32-bit fixed point, truncated to 23 bits. */
+/* A group scale as it is stored, returned as the fp32 value it represents:
+ * fp32 unchanged; binary16 keeps 11 significant bits (quantum 2^(e-10) in the
+ * binade [2^e, 2^(e+1)), e >= -14, so 2^-24 below 2^-14) rounded to nearest,
+ * ties to even, and values beyond 65504 after rounding become infinity;
+ * bfloat16 keeps the upper 16 bits of the fp32 pattern, rounded to nearest,
+ * ties to even on the discarded 16 bits. */
+static float scale_as_stored(float s, int fmt) {
+  if (fmt == LSQO_SCALE_F16) {
+    if (s == 0.0f || !isfinite(s)) return s;
+    int e;
+    frexp((double)s, &e);                       /* |s| = m 2^e, 0.5 <= m < 1 */
+    const int lowest = (e - 1 < -14 ? -14 : e - 1) - 10;   /* exponent of the last kept bit */
+    const double v = ldexp(round_half_even(ldexp((double)s, -lowest)), lowest);
+    return fabs(v) > 65504.0 ? copysignf(INFINITY, s) : (float)v;
+  }
+  if (fmt == LSQO_SCALE_BF16) {
+    uint32_t u;
+    memcpy(&u, &s, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u) return s;       /* infinity or NaN */
+    uint32_t keep = u >> 16;
+    const uint32_t rest = u & 0xFFFFu;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;
+    u = keep << 16;
+    float r;
+    memcpy(&r, &u, sizeof r);
+    return r;
+  }
+  return s;
+}
+
+float lsqo_scale_as_stored(float s, int32_t fmt) { return scale_as_stored(s, fmt); }
+
 static double weyl_dither(int64_t step, int dv, int dk, int r, int c) {
   const uint32_t i = (uint32_t)((uint64_t)step * (uint64_t)dv * (uint64_t)dk +
                                 (uint64_t)r * (uint64_t)dk + (uint64_t)c);
@@ -189,7 +227,7 @@ static void step_heads(step_job* J) {
             float a = fabsf(src[c]);
             if (a > amax) amax = a;
           }
-          snew = amax / (float)qm;
+          snew = scale_as_stored(amax / (float)qm, cfg->scale_fmt);
         }
         float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
         for (int c = gi * g; c < (gi + 1) * g; ++c) {
@@ -453,7 +491,7 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
             float av = fabsf(x[c]);
             if (av > amax) amax = av;
           }
-          snew = amax / (float)qm;
+          snew = scale_as_stored(amax / (float)qm, cfg->scale_fmt);
         }
         const float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
         requantise_group(cfg, i, gi * g, (gi + 1) * g, x, sp, sig, inv, C, &st,
@@ -548,7 +586,7 @@ int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes
               float a = fabsf(x[c]);
               if (a > amax) amax = a;
             }
-            snew = amax / (float)qm;
+            snew = scale_as_stored(amax / (float)qm, cfg->scale_fmt);
           }
           const float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
           for (int c = gi * g; c < (gi + 1) * g; ++c) {
@@ -584,7 +622,7 @@ int lsqo_calibrate(const lsqo_config* cfg, const float* S, int8_t* codes, float*
         float a = fabsf(x[c]);
         if (a > amax) amax = a;
       }
-      float s = amax / (float)qm;
+      float s = scale_as_stored(amax / (float)qm, cfg->scale_fmt);
       float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
       for (int c = gi * g; c < (gi + 1) * g; ++c) {
         double y = (double)x[c] * (double)inv;

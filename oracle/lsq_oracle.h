@@ -67,7 +67,9 @@
  *
  * State layout used by the oracle (unpacked, host memory, heads = batch*heads):
  *   codes  int8  [heads][Dv][Dk]        signed codes in [-qmax, qmax]
- *   scales float [heads][Dv][Dk/group]  one fp32 scale per group along Dk
+ *   scales float [heads][Dv][Dk/group]  one scale per group along Dk, an fp32
+ *                                       value exactly representable in the
+ *                                       configured storage format
  *   ref    float [heads][Dv][Dk]        fp32 reference state (yoked policy)
  *   f32    float [heads][Dv][Dk]        fp32 state (bits == 32)
  * Inputs: q,k [heads][Dk]; v [heads][Dv]; alpha [heads] (scalar decay) or
@@ -86,6 +88,7 @@ extern "C" {
 enum { LSQO_POLICY_NONE = 0, LSQO_POLICY_DYNAMIC = 1, LSQO_POLICY_PERSISTENT = 2, LSQO_POLICY_YOKED = 3 };
 enum { LSQO_ROUND_RNE = 0, LSQO_ROUND_BDR = 1, LSQO_ROUND_DITHER = 2 };
 enum { LSQO_DECAY_SCALAR = 0, LSQO_DECAY_DIAG = 1 };
+enum { LSQO_SCALE_F32 = 0, LSQO_SCALE_F16 = 1, LSQO_SCALE_BF16 = 2 };
 
 typedef struct {
   int32_t batch, heads, dk, dv;
@@ -96,6 +99,8 @@ typedef struct {
   int32_t delta;    /* 0: linear write, 1: delta-rule correction */
   int32_t decay;    /* LSQO_DECAY_* */
   int32_t lrb_rank; /* Low-Rank Bypass slots r (0: off; lsqo_step_lrb only) */
+  int32_t scale_fmt; /* LSQO_SCALE_*: stored format of the group scales (the
+                        host arrays stay float, holding values of that format) */
   int64_t step;     /* sequence position of the (first) step: dithered rounding,
                        and the bypass slot (step mod r) */
 } lsqo_config;
@@ -109,6 +114,9 @@ typedef struct {
 
 /* 0 on success, -1 on an invalid configuration */
 int lsqo_check_config(const lsqo_config* cfg);
+
+/* A group scale as stored in format fmt (LSQO_SCALE_*), as an fp32 value. */
+float lsqo_scale_as_stored(float s, int32_t fmt);
 
 /* One decode step for every head, in place.  o_ref (nullable) receives the
  * yoked reference readout R_t q_t. */
