@@ -188,7 +188,8 @@ def main() -> int:
                 "speedup_of_quantised_step": round(fms / (wall * 1e3 / K), 3),
                 "state_memory_ratio": round(
                     sum(f.f32.numel() * 4 for _, f in fl)
-                    / sum(a["st"].codes.numel() + a["st"].scales.numel() * 4 for a in arms), 3)}
+                    / sum(a["st"].codes.numel() + a["st"].scales.numel() * a["st"].scales.element_size()
+                          for a in arms), 3)}
         del fl
         log(f"fp32-state step {fms:.3f} ms")
 

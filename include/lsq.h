@@ -56,7 +56,8 @@
  *          c, two's-complement nibble.  Codes lie in [-qmax, qmax]; the
  *          most negative code (-8, -128) is never produced and is not a
  *          valid input.
- *   scales [heads][Dv][Dk/group] fp32, one per contiguous group along Dk.
+ *   scales [heads][Dv][Dk/group], one per contiguous group along Dk: fp32,
+ *          or (scale_fmt) IEEE binary16 or bfloat16 bit patterns, 2 bytes.
  *   ref    [heads][Dv][Dk] fp32, the yoked policy's reference state.
  *   f32    [heads][Dv][Dk] fp32, the state of the unquantised mode (bits 32).
  *   lrb    Low-Rank Bypass buffer (lrb_rank = r > 0), fp32: a [heads][r][Dv]
@@ -119,6 +120,7 @@ typedef enum {
 
 typedef enum { LSQ_ROUND_RNE = 0, LSQ_ROUND_BDR = 1, LSQ_ROUND_DITHER = 2 } lsq_rounding;
 typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
+typedef enum { LSQ_SCALE_F32 = 0, LSQ_SCALE_F16 = 1, LSQ_SCALE_BF16 = 2 } lsq_scale_format;
 
 /* Shape, format and method flags of one handle.
  *   bits   4, 8 (quantised) or 32 (fp32 state, policy NONE)
@@ -129,11 +131,24 @@ typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
  *          groups and fp32 scales stores 6 bits per element, 5.33x less
  *          than an fp32 state.
  *   delta  0: linear write, 1: delta-rule correction
+ *   scale_fmt  stored format of the group scales (the pages fix none; 16-bit
+ *          scales are the scale-format variant of "Preserving Updates in
+ *          Low-Bit Recurrent State Quantization", whose "up to 5.3x" memory
+ *          figure leaves the format open).  A computed scale (dynamic, yoked,
+ *          calibration) is rounded to the format, to nearest with ties to
+ *          even (binary16 with subnormals, overflow to infinity; bfloat16 on
+ *          the upper half of the fp32 pattern), and the codes are formed with
+ *          that stored value: inv = fl(1/s_stored); elements beyond qmax
+ *          steps of a scale that rounded down clamp.  Quantised states only;
+ *          not with the bypass or lsq_prefill.  INT4 g32 with bfloat16
+ *          scales stores 4.5 bits per element (7.1x less than fp32), INT4
+ *          g16 5 bits (6.4x).
  */
 typedef struct {
   int32_t batch, heads, dk, dv;
   int32_t bits, group, policy, rounding, delta, decay;
   int32_t lrb_rank;   /* Low-Rank Bypass slots r, 0 (off) to 8; see below */
+  int32_t scale_fmt;  /* lsq_scale_format (LSQ_SCALE_F32 = 0) */
 } lsq_config;
 
 /* Caller-owned device buffers and their capacities in bytes.  Buffers the

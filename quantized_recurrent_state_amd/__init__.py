@@ -17,6 +17,7 @@ from ._lib import LsqError
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
 ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
 DECAY_SCALAR, DECAY_DIAG = 0, 1
+SCALE_F32, SCALE_F16, SCALE_BF16 = 0, 1, 2
 
 __all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_alloc",
            "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_set_calibrated",
@@ -38,6 +39,7 @@ class LsqConfig:
     delta: int = 0
     decay: int = DECAY_SCALAR
     lrb_rank: int = 0       # Low-Rank Bypass slots (0: off)
+    scale_fmt: int = SCALE_F32   # stored group-scale format
 
     @property
     def n(self) -> int:
@@ -147,8 +149,9 @@ class LsqState:
         if cfg.bits != 32:
             self.codes = torch.empty((n, dv, dk * cfg.bits // 8), dtype=torch.uint8,
                                      device=self.device)
-            self.scales = torch.empty((n, dv, dk // cfg.group), dtype=torch.float32,
-                                      device=self.device)
+            sdt = {SCALE_F32: torch.float32, SCALE_F16: torch.float16,
+                   SCALE_BF16: torch.bfloat16}[cfg.scale_fmt]
+            self.scales = torch.empty((n, dv, dk // cfg.group), dtype=sdt, device=self.device)
         if n_ref:
             self.ref = torch.empty((n, dv, dk), dtype=torch.float32, device=self.device)
         if cfg.bits == 32:

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "LSQ_OK", 1: "LSQ_ERR_INVALID_ARG", 2: "LSQ_ERR_UNSUPPORTED",
 class lsq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "heads", "dk", "dv", "bits", "group", "policy", "rounding", "delta",
-                 "decay", "lrb_rank")]
+                 "decay", "lrb_rank", "scale_fmt")]
 
 
 class lsq_buffers(ctypes.Structure):

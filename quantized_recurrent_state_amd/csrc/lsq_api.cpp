@@ -79,6 +79,11 @@ lsq_status check_config(const lsq_config* c) {
                   "group %d: this build needs a power-of-two group of at least %d elements",
                   c->group, min_group);
   }
+  if (c->scale_fmt != LSQ_SCALE_F32 && c->scale_fmt != LSQ_SCALE_F16 &&
+      c->scale_fmt != LSQ_SCALE_BF16)
+    return fail(LSQ_ERR_INVALID_ARG, "scale_fmt must be F32, F16 or BF16");
+  if (c->bits == 32 && c->scale_fmt != LSQ_SCALE_F32)
+    return fail(LSQ_ERR_INVALID_ARG, "an fp32 state has no scales (scale_fmt F32)");
   if (c->lrb_rank < 0 || c->lrb_rank > 8)
     return fail(LSQ_ERR_INVALID_ARG, "lrb_rank must be 0 to 8");
   if (c->lrb_rank > 0) {
@@ -87,6 +92,8 @@ lsq_status check_config(const lsq_config* c) {
       return fail(LSQ_ERR_UNSUPPORTED, "the bypass supports the DYNAMIC and PERSISTENT policies");
     if (c->group < 32)
       return fail(LSQ_ERR_UNSUPPORTED, "the bypass needs groups of 32 or more elements");
+    if (c->scale_fmt != LSQ_SCALE_F32)
+      return fail(LSQ_ERR_UNSUPPORTED, "the bypass keeps fp32 scales");
   }
   const lsq::Geometry g = lsq::geometry(c->bits, c->dk);
   const int64_t iters = (c->dv + g.rows_per_iter - 1) / g.rows_per_iter;
@@ -105,7 +112,7 @@ void sizes_of(const lsq_config& c, size_t (&sz)[kBuffers]) {
     return;
   }
   sz[0] = elems * c.bits / 8;
-  sz[1] = (size_t)n_heads(c) * c.dv * (c.dk / c.group) * 4;
+  sz[1] = (size_t)n_heads(c) * c.dv * (c.dk / c.group) * (c.scale_fmt == LSQ_SCALE_F32 ? 4 : 2);
   if (c.policy == LSQ_POLICY_YOKED) sz[2] = elems * 4;
   if (c.lrb_rank > 0) sz[4] = (size_t)n_heads(c) * c.lrb_rank * (c.dv + 2 * (size_t)c.dk) * 4;
 }
@@ -148,6 +155,7 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
   lsq::StepArgs a{};
   a.codes = static_cast<uint8_t*>(st->codes);
   a.scales = st->scales;
+  a.sfmt = st->cfg.scale_fmt;
   a.ref = (c.bits == 32) ? st->f32 : st->ref;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.o = o;
   a.o_ref = (c.policy == LSQ_POLICY_YOKED) ? o_ref : nullptr;
@@ -172,6 +180,10 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
     e = lsq::launch_lrb_step(a, c.bits, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   } else if (c.bits == 32)
     e = lsq::launch_step_f32(a, c.dk, c.delta, c.decay, stream);
+  else if (c.scale_fmt != LSQ_SCALE_F32)
+    e = (c.bits == 4 ? (c.scale_fmt == LSQ_SCALE_F16 ? lsq::launch_step_q4_f16 : lsq::launch_step_q4_bf16)
+                     : (c.scale_fmt == LSQ_SCALE_F16 ? lsq::launch_step_q8_f16 : lsq::launch_step_q8_bf16))(
+        a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   else if (c.bits == 4)
     e = lsq::launch_step_q4(a, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   else
@@ -276,6 +288,7 @@ lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream) {
   a.S = S;
   a.codes = static_cast<uint8_t*>(st->codes);
   a.scales = st->scales;
+  a.sfmt = st->cfg.scale_fmt;
   a.ref = (c.policy == LSQ_POLICY_YOKED) ? st->ref : nullptr;
   a.n_heads = (int32_t)n_heads(c);
   a.dv = c.dv;
@@ -357,6 +370,7 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
     return fail(LSQ_ERR_UNSUPPORTED, "prefill supports the DYNAMIC and PERSISTENT policies");
   if (c.delta != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill supports the linear write (delta 0)");
   if (c.lrb_rank != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill does not take the bypass");
+  if (c.scale_fmt != LSQ_SCALE_F32) return fail(LSQ_ERR_UNSUPPORTED, "prefill keeps fp32 scales");
   if (c.dv != 64 && c.dv != 128)
     return fail(LSQ_ERR_UNSUPPORTED, "dv %d: prefill has dv 64 and 128", c.dv);
   if (c.dk / c.group > 8) return fail(LSQ_ERR_UNSUPPORTED, "prefill holds at most 8 groups per row");

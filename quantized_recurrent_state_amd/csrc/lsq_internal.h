@@ -11,7 +11,7 @@ namespace lsq {
 // Arguments of one decode-step launch (one handle, one step).
 struct StepArgs {
   uint8_t* codes;        // [n][dv][dk*bits/8]
-  float* scales;         // [n][dv][ng]
+  float* scales;         // [n][dv][ng]: fp32, or 16-bit patterns when sfmt != 0
   float* ref;            // [n][dv][dk]  yoked reference (or fp32 state for bits 32)
   const float* q;        // [n][dk]
   const float* k;        // [n][dk]
@@ -38,6 +38,7 @@ struct StepArgs {
   int32_t lrb_used;      // slots filled before this step (step mod r)
   int32_t lrb_merge;     // 1 when this step fills the last slot and merges
   int32_t lrb_cin, lrb_cout;  // b copy read / written this step
+  int32_t sfmt;          // stored scale format: 0 fp32, 1 binary16, 2 bfloat16
 };
 
 // Arguments of a calibration launch: quantise an fp32 state into codes/scales.
@@ -48,6 +49,7 @@ struct CalibArgs {
   float* ref;            // copy of S for the yoked policy, else null
   int32_t n_heads, dv, group, ng;
   int32_t nit, waves_per_head, total_waves;
+  int32_t sfmt;          // stored scale format (as StepArgs)
 };
 
 // Arguments of a chunkwise prefill launch (linear write): the handle's packed
@@ -76,6 +78,14 @@ hipError_t launch_step_q4(const StepArgs& a, int dk, int policy, int rounding, i
                           hipStream_t s);
 hipError_t launch_step_q8(const StepArgs& a, int dk, int policy, int rounding, int delta, int diag,
                           hipStream_t s);
+hipError_t launch_step_q4_f16(const StepArgs& a, int dk, int policy, int rounding, int delta,
+                              int diag, hipStream_t s);
+hipError_t launch_step_q4_bf16(const StepArgs& a, int dk, int policy, int rounding, int delta,
+                               int diag, hipStream_t s);
+hipError_t launch_step_q8_f16(const StepArgs& a, int dk, int policy, int rounding, int delta,
+                              int diag, hipStream_t s);
+hipError_t launch_step_q8_bf16(const StepArgs& a, int dk, int policy, int rounding, int delta,
+                               int diag, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs& a, int dk, int delta, int diag, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s);
 hipError_t launch_lrb_step(const StepArgs& a, int bits, int dk, int policy, int rounding,

@@ -113,9 +113,14 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
     for (int e = 0; e < EPL; ++e)
       amax[GPL == 2 ? e / 16 : 0] = fmaxf(amax[GPL == 2 ? e / 16 : 0], fabsf(x[e]));
     float s[GPL], inv[GPL];
+    uint32_t s16[GPL] = {};
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
       s[g] = (GPL == 2 ? amax[g] : group_max(amax[g], gl)) / F::QMAX;
+      if (a.sfmt != SFMT_F32) {          // codes are formed with the stored scale
+        s16[g] = scale_to16(s[g], a.sfmt);
+        s[g] = scale_from16(s16[g], a.sfmt);
+      }
       inv[g] = inv_scale(s[g]);
     }
     float t[EPL];
@@ -131,7 +136,13 @@ __global__ __launch_bounds__(256) void calibrate_kernel(CalibArgs a) {
       for (int c = 0; c < F::NW / 4; ++c)
         reinterpret_cast<uint4*>(p)[c] = make_uint4(X[4 * c] ^ F::OFF, X[4 * c + 1] ^ F::OFF,
                                                     X[4 * c + 2] ^ F::OFF, X[4 * c + 3] ^ F::OFF);
-      if constexpr (GPL == 2) {
+      if (a.sfmt != SFMT_F32) {
+        uint16_t* s16p = reinterpret_cast<uint16_t*>(a.scales) + row * a.ng + gi;
+        if constexpr (GPL == 2)
+          *reinterpret_cast<uint32_t*>(s16p) = s16[0] | (s16[1] << 16);
+        else if ((lc % gl) == 0)
+          *s16p = (uint16_t)s16[0];
+      } else if constexpr (GPL == 2) {
         *reinterpret_cast<float2*>(a.scales + row * a.ng + gi) = make_float2(s[0], s[1]);
       } else {
         if ((lc % gl) == 0) a.scales[row * a.ng + gi] = s[0];

@@ -39,6 +39,7 @@
 // same xor-add.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -357,10 +358,28 @@ __device__ __forceinline__ void store_codes16(uint8_t* p, u32x4 v) {
 }
 
 // Per-lane row data, loaded one iteration ahead.
+// Stored group-scale formats.  A 16-bit scale converts to fp32 exactly; an
+// fp32 scale is rounded to the stored format to nearest, ties to even
+// (binary16 by the conversion instruction in the default rounding mode, with
+// subnormals; bfloat16 by rounding the discarded 16 bits of the pattern).
+enum { SFMT_F32 = 0, SFMT_F16 = 1, SFMT_BF16 = 2 };
+
+__device__ __forceinline__ float scale_from16(uint32_t bits16, int sfmt) {
+  return sfmt == SFMT_F16 ? __half2float(__ushort_as_half((unsigned short)bits16))
+                          : __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t scale_to16(float s, int sfmt) {
+  if (sfmt == SFMT_F16) return __half_as_ushort(__float2half_rn(s));
+  const uint32_t u = __float_as_uint(s);             // finite, non-negative
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <int BITS, int GPL>
 struct RowIn {
   uint32_t x[Fmt<BITS>::NW];
   float s[GPL];       // the lane's group scale(s)
+  uint32_t sw;        // 16-bit scale pattern(s) as loaded, converted just before use
   float v;
 };
 
@@ -388,7 +407,7 @@ __device__ __forceinline__ const T& at_bytes(const T* base, uint32_t byte_off) {
 
 template <int BITS, int DK, int GPL>
 __device__ __forceinline__ void load_row(RowIn<BITS, GPL>& R, const HeadPtrs& H, int ng, uint32_t r,
-                                         int lc, int gi) {
+                                         int lc, int gi, int sfmt = SFMT_F32) {
   constexpr int ROWB = DK * BITS / 8;
   const uint8_t* p = H.codes + (r * ROWB + lc * (EPL * BITS / 8));
 #pragma unroll
@@ -399,14 +418,33 @@ __device__ __forceinline__ void load_row(RowIn<BITS, GPL>& R, const HeadPtrs& H,
     R.x[4 * c + 2] = w.z;
     R.x[4 * c + 3] = w.w;
   }
-  if constexpr (GPL == 2) {
-    const float2 s2 = at_bytes(reinterpret_cast<const float2*>(H.scales), (r * ng + gi) * 4u);
-    R.s[0] = s2.x;
-    R.s[1] = s2.y;
+  if (sfmt == SFMT_F32) {
+    if constexpr (GPL == 2) {
+      const float2 s2 = at_bytes(reinterpret_cast<const float2*>(H.scales), (r * ng + gi) * 4u);
+      R.s[0] = s2.x;
+      R.s[1] = s2.y;
+    } else {
+      R.s[0] = at_bytes(H.scales, (r * ng + gi) * 4u);
+    }
+  } else if constexpr (GPL == 2) {       // both 16-bit scales in one dword
+    R.sw = at_bytes(reinterpret_cast<const uint32_t*>(H.scales), (r * ng + gi) * 2u);
   } else {
-    R.s[0] = at_bytes(H.scales, (r * ng + gi) * 4u);
+    R.sw = at_bytes(reinterpret_cast<const uint16_t*>(H.scales), (r * ng + gi) * 2u);
   }
   R.v = at_bytes(H.v, r * 4u);
+}
+
+// 16-bit scales of a prefetched row to fp32, right before the row is used (a
+// conversion next to the load would wait for it).
+template <int BITS, int GPL>
+__device__ __forceinline__ void resolve_scales(RowIn<BITS, GPL>& R, int sfmt) {
+  if (sfmt == SFMT_F32) return;
+  if constexpr (GPL == 2) {
+    R.s[0] = scale_from16(R.sw & 0xFFFFu, sfmt);
+    R.s[1] = scale_from16(R.sw >> 16, sfmt);
+  } else {
+    R.s[0] = scale_from16(R.sw, sfmt);
+  }
 }
 
 // fl(1/s): v_rcp_f32 followed by one fma Newton step reproduces the correctly
@@ -479,9 +517,12 @@ __device__ __forceinline__ void lds_words(uint32_t (&d)[N], const float* lds, in
 
 // The row loop of one wave.  KZ: the head's key has a zero component (no
 // update direction there), so those elements drop their round-up candidate.
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, bool KZ>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF, bool KZ>
 __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DIAG>& L,
                                          const float* vec) {
+  // stored scale format, fixed per instance (SFMT_*): the other formats'
+  // paths are compiled out
+  constexpr int sfmt = SF;
   // vec + L.vbase + v*DK + L.col0: this lane's 32 columns of vector v
   const int base0 = L.vbase + L.col0;
   using P = LdsPlan<BITS, DK, ROUND>;
@@ -650,6 +691,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
     };
 
     float snew[GPL];
+    uint32_t s16[GPL] = {};
 #pragma unroll
     for (int h = 0; h < GPL; ++h) snew[h] = in.s[h];
     float po = 0.f;
@@ -724,6 +766,13 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
         } else {
           snew[0] = group_max(amax[0], L.gl) / F::QMAX;
         }
+        if (sfmt != SFMT_F32) {            // the stored value forms the codes
+#pragma unroll
+          for (int h = 0; h < GPL; ++h) {
+            s16[h] = scale_to16(snew[h], sfmt);
+            snew[h] = scale_from16(s16[h], sfmt);
+          }
+        }
       }
       float inv[GPL];
 #pragma unroll
@@ -760,11 +809,18 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       for (int c = 0; c < NW / 4; ++c)
         store_codes16(p + 16 * c, u32x4{X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]});
       if constexpr (POLICY != POL_PERSISTENT) {
-        if constexpr (GPL == 2)
-          at_bytes(reinterpret_cast<float2*>(H.scales), (row * a.ng + L.gi) * 4u) =
-              make_float2(snew[0], snew[1]);
-        else if ((L.lc % L.gl) == 0)
-          at_bytes(H.scales, (row * a.ng + L.gi) * 4u) = snew[0];
+        if (sfmt == SFMT_F32) {
+          if constexpr (GPL == 2)
+            at_bytes(reinterpret_cast<float2*>(H.scales), (row * a.ng + L.gi) * 4u) =
+                make_float2(snew[0], snew[1]);
+          else if ((L.lc % L.gl) == 0)
+            at_bytes(H.scales, (row * a.ng + L.gi) * 4u) = snew[0];
+        } else if constexpr (GPL == 2) {
+          at_bytes(reinterpret_cast<uint32_t*>(H.scales), (row * a.ng + L.gi) * 2u) =
+              s16[0] | (s16[1] << 16);
+        } else if ((L.lc % L.gl) == 0) {
+          at_bytes(reinterpret_cast<uint16_t*>(H.scales), (row * a.ng + L.gi) * 2u) = (uint16_t)s16[0];
+        }
       }
     }
   };
@@ -773,23 +829,25 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
   RowIn<BITS, GPL> bufA, bufB;
   bool liveA, liveB;
   uint32_t rowA = row_of(0, liveA), rowB = 0;
-  load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi);
+  load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
   for (int it = 0; it < a.nit; it += 2) {
     if (it + 1 < a.nit) {
       rowB = row_of(it + 1, liveB);
-      load_row<BITS, DK, GPL>(bufB, H, a.ng, rowB, L.lc, L.gi);
+      load_row<BITS, DK, GPL>(bufB, H, a.ng, rowB, L.lc, L.gi, sfmt);
     }
+    resolve_scales(bufA, sfmt);
     process(bufA, liveA, rowA);
     if (it + 1 >= a.nit) break;
     if (it + 2 < a.nit) {
       rowA = row_of(it + 2, liveA);
-      load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi);
+      load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
     }
+    resolve_scales(bufB, sfmt);
     process(bufB, liveB, rowB);
   }
 }
 
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSQ_STEP_WAVES_PER_EU)))
 void step_kernel(StepArgs a) {
   using F = Fmt<BITS>;
@@ -808,7 +866,8 @@ void step_kernel(StepArgs a) {
   {
     const size_t row0 = (size_t)L.h * a.dv;
     L.H.codes = a.codes + row0 * (DK * BITS / 8);
-    L.H.scales = a.scales + row0 * a.ng;
+    L.H.scales = reinterpret_cast<float*>(reinterpret_cast<char*>(a.scales) +
+                                          row0 * a.ng * (SF ? 2 : 4));
     L.H.v = a.v + row0;
     L.H.o = a.o + row0;
     L.H.o_ref = a.o_ref ? a.o_ref + row0 : nullptr;
@@ -900,27 +959,28 @@ void step_kernel(StepArgs a) {
 
   if constexpr (BDR) {
     if (__any(kzero))
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, true>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, true>(a, L, vec);
     else
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, false>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false>(a, L, vec);
   } else {
-    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, false>(a, L, vec);
+    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false>(a, L, vec);
   }
 }
 
 // Dispatch one (BITS, DK) family over the method flags and the group size
 // (16-element groups: two groups per lane; 32 and more: one).
-template <int BITS, int DK>
+template <int BITS, int DK, int SF>
 hipError_t launch_family(const StepArgs& a, int policy, int rounding, int delta, int diag,
                          hipStream_t s) {
+  static_assert(SF == SFMT_F32 || SF == SFMT_F16 || SF == SFMT_BF16, "stored scale format");
   const dim3 grid((a.total_waves + 3) / 4), block(256);
   const int gpl = a.group < EPL ? 2 : 1;   // 16-element groups: two per lane
 #define LSQ_CASE(P, R, D, G)                                                               \
   if (policy == P && rounding == R && delta == D && diag == G) {                           \
     if (gpl == 2)                                                                          \
-      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 2>), grid, block, 0, s, a);    \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 2, SF>), grid, block, 0, s, a); \
     else                                                                                   \
-      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 1>), grid, block, 0, s, a);    \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 1, SF>), grid, block, 0, s, a); \
     return hipGetLastError();                                                              \
   }
 #define LSQ_CASES_PR(P, R) \

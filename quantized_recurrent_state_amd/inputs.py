@@ -128,6 +128,7 @@ class Arm:
     rounding: int
     layers: tuple = (0,)   # layer indices folded into the batch; seeds are per layer
     lrb_rank: int = 0      # Low-Rank Bypass slots (0: off)
+    scale_fmt: int = 0     # stored group-scale format: 0 fp32, 1 binary16, 2 bfloat16
 
 
 @dataclass(frozen=True)
@@ -149,7 +150,8 @@ class Workload:
     def arm_config(self, arm: Arm) -> dict:
         return dict(batch=self.batch * len(arm.layers), heads=self.heads, dk=self.dk, dv=self.dv,
                     bits=arm.bits, group=arm.group, policy=arm.policy, rounding=arm.rounding,
-                    delta=self.delta, decay=self.decay, lrb_rank=arm.lrb_rank)
+                    delta=self.delta, decay=self.decay, lrb_rank=arm.lrb_rank,
+                    scale_fmt=arm.scale_fmt)
 
 
 WORKLOADS = {
@@ -183,14 +185,14 @@ WORKLOADS = {
 
 
 def _stack24_variant(key: str, name: str, rounding: int, int4_group: int,
-                     lrb_rank: int = 0) -> Workload:
+                     lrb_rank: int = 0, scale_fmt: int = 0) -> Workload:
     base = WORKLOADS["stack24"]
     return Workload(name, base.recipe, base.batch, base.heads, base.dk, base.dv, base.delta,
                     base.decay, base.steps, base.warmup,
                     (Arm("layers0-3-int8g64", 8, 64, POLICY_PERSISTENT, rounding, tuple(range(0, 4)),
-                         lrb_rank),
+                         lrb_rank, scale_fmt),
                      Arm(f"layers4-23-int4g{int4_group}", 4, int4_group, POLICY_PERSISTENT, rounding,
-                         tuple(range(4, 24)), lrb_rank)),
+                         tuple(range(4, 24)), lrb_rank, scale_fmt)),
                     shared_inputs=False)
 
 
@@ -202,6 +204,14 @@ WORKLOADS["stack24-dither"] = _stack24_variant(
     "stack24-dither", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-dither", ROUND_DITHER, 32)
 WORKLOADS["stack24-g16"] = _stack24_variant(
     "stack24-g16", "gdn24-512x32-128x128-mixed-int8g64-int4g16-persistent-bdr", ROUND_BDR, 16)
+# ... with bfloat16 group scales (INT4 g32: 4.5 bits per element), and with INT4 g16 and
+# bfloat16 scales (5 bits per element)
+WORKLOADS["stack24-bf16"] = _stack24_variant(
+    "stack24-bf16", "gdn24-512x32-128x128-mixed-int8g64-int4g32-bf16scale-persistent-bdr", ROUND_BDR,
+    32, scale_fmt=2)
+WORKLOADS["stack24-g16-bf16"] = _stack24_variant(
+    "stack24-g16-bf16", "gdn24-512x32-128x128-mixed-int8g64-int4g16-bf16scale-persistent-bdr",
+    ROUND_BDR, 16, scale_fmt=2)
 # ... and with a rank-4 Low-Rank Bypass in every layer
 WORKLOADS["stack24-lrb4"] = _stack24_variant(
     "stack24-lrb4", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-bdr-lrb4", ROUND_BDR, 32,

@@ -64,7 +64,8 @@ def algorithmic_bytes(cfg: LsqConfig, with_o_ref: bool = False) -> int:
         state = 2 * 4 * dv * dk
     else:
         state = 2 * dv * dk * cfg.bits // 8
-        state += dv * (dk // cfg.group) * 4 * (2 if cfg.policy in (POLICY_DYNAMIC, POLICY_YOKED) else 1)
+        sbytes = 4 if cfg.scale_fmt == 0 else 2
+        state += dv * (dk // cfg.group) * sbytes * (2 if cfg.policy in (POLICY_DYNAMIC, POLICY_YOKED) else 1)
         if cfg.policy == POLICY_YOKED:
             state += 2 * 4 * dv * dk
     ins = 4 * (2 * dk + dv + (dk if cfg.decay == DECAY_DIAG else 1) + 1)

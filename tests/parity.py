@@ -14,6 +14,11 @@ Bar (taken from the decode-step contract):
     for dithered rounding the integers against y + u); such cases are counted
     and reported;
   * dynamic and yoked scales within 1e-6 relative, persistent scales exact;
+    16-bit stored scales (binary16, bfloat16) equal, or under the delta rule
+    adjacent values of the format (the fp32 scale before rounding may sit at
+    the format's rounding midpoint and then follows the dot product's
+    summation order); such a group's codes are not compared and the group is
+    counted (excused_groups);
   * outputs o (and o_ref) with ||o_gpu - o_oracle||_inf <= 1e-4 ||o_oracle||_inf
     per head;
   * the yoked fp32 reference state within 1e-5 of its own row norm.
@@ -41,7 +46,8 @@ def ocfg_of(cfg, step: int = 0) -> OracleConfig:
     handle's step index before the step (the dither's sequence position)."""
     return OracleConfig(batch=cfg.batch, heads=cfg.heads, dk=cfg.dk, dv=cfg.dv, bits=cfg.bits,
                         group=cfg.group, policy=cfg.policy, rounding=cfg.rounding,
-                        delta=cfg.delta, decay=cfg.decay, step=step)
+                        delta=cfg.delta, decay=cfg.decay, step=step,
+                        scale_fmt=cfg.scale_fmt)
 
 
 def snapshot(gpu_state, heads=None) -> OracleState:
@@ -51,7 +57,7 @@ def snapshot(gpu_state, heads=None) -> OracleState:
     st = OracleState()
     if gpu_state.codes is not None:
         st.codes = oracle.unpack(sel(gpu_state.codes).cpu().numpy(), cfg.bits, cfg.dk)
-        st.scales = sel(gpu_state.scales).cpu().numpy().copy()
+        st.scales = sel(gpu_state.scales).float().cpu().numpy().copy()
     if gpu_state.ref is not None:
         st.ref = sel(gpu_state.ref).cpu().numpy().copy()
     if gpu_state.f32 is not None:
@@ -71,10 +77,13 @@ class Report:
     max_ref_rel: float = 0.0
     bdr_fired: int = 0
     clamped: int = 0
+    excused_groups: int = 0
+    groups: int = 0
     notes: list = field(default_factory=list)
 
     def add(self, o: "Report"):
-        for k in ("codes", "exact", "excused", "failed", "bdr_fired", "clamped"):
+        for k in ("codes", "exact", "excused", "failed", "bdr_fired", "clamped", "excused_groups",
+                  "groups"):
             setattr(self, k, getattr(self, k) + getattr(o, k))
         for k in ("max_o_rel", "max_oref_rel", "max_scale_rel", "max_ref_rel"):
             setattr(self, k, max(getattr(self, k), getattr(o, k)))
@@ -89,7 +98,8 @@ class Report:
         return (f"codes={self.codes} exact={self.exact} excused={self.excused} "
                 f"failed={self.failed} o_rel={self.max_o_rel:.2e} oref_rel={self.max_oref_rel:.2e} "
                 f"scale_rel={self.max_scale_rel:.2e} ref_rel={self.max_ref_rel:.2e} "
-                f"bdr={self.bdr_fired} clamped={self.clamped} {self.notes[:3]}")
+                f"bdr={self.bdr_fired} clamped={self.clamped} "
+                f"excused_groups={self.excused_groups}/{self.groups} {self.notes[:3]}")
 
 
 def _normwise(got, want):
@@ -100,6 +110,14 @@ def _normwise(got, want):
     den = np.abs(want).max(axis=1)
     rel = np.where(den > 0, num / np.where(den > 0, den, 1), np.where(num > 0, np.inf, 0))
     return float(rel.max()) if rel.size else 0.0
+
+
+def _bits16(scales, fmt):
+    """16-bit patterns of scales held as fp32 values of a 16-bit format."""
+    x = np.ascontiguousarray(scales, np.float32)
+    if fmt == 1:
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def boundary_distance(y, yp, codes_oracle, rounding):
@@ -137,7 +155,19 @@ def compare_step(ocfg: OracleConfig, before: OracleState, inputs, gpu_after: Ora
         if gpu_o_ref is not None:
             rep.max_oref_rel = _normwise(np.asarray(gpu_o_ref), o_ref)
     # scales
-    if ocfg.policy == POLICY_PERSISTENT:
+    skip = np.zeros(st.codes.shape, bool)      # elements of excused groups
+    rep.groups = st.scales.size
+    if getattr(ocfg, "scale_fmt", 0) and ocfg.policy != POLICY_PERSISTENT:
+        g16 = _bits16(gpu_after.scales, ocfg.scale_fmt)
+        w16 = _bits16(st.scales, ocfg.scale_fmt)
+        diff = g16 != w16
+        adjacent = np.abs(g16.astype(np.int64) - w16.astype(np.int64)) == 1
+        if np.any(diff & ~adjacent) or (np.any(diff) and ocfg.delta == 0):
+            rep.max_scale_rel = np.inf
+            rep.notes.append(f"16-bit scales differ at {np.argwhere(diff)[:3].tolist()}")
+        rep.excused_groups = int(diff.sum())
+        skip = np.repeat(diff, ocfg.group, axis=-1)
+    elif ocfg.policy == POLICY_PERSISTENT:
         if not np.array_equal(gpu_after.scales, st.scales):
             rep.max_scale_rel = np.inf
             rep.notes.append("persistent scales changed")
@@ -147,8 +177,8 @@ def compare_step(ocfg: OracleConfig, before: OracleState, inputs, gpu_after: Ora
         rel = np.where(den > 0, num / np.where(den > 0, den, 1), np.where(num > 0, np.inf, 0))
         rep.max_scale_rel = float(rel.max()) if rel.size else 0.0
     # codes
-    rep.codes = st.codes.size
-    diff = gpu_after.codes != st.codes
+    rep.codes = st.codes.size - int(skip.sum())
+    diff = (gpu_after.codes != st.codes) & ~skip
     nd = int(diff.sum())
     rep.exact = rep.codes - nd
     if nd:

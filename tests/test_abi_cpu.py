@@ -34,6 +34,11 @@ def test_every_declared_symbol_is_exported():
     (lsq.LsqConfig(1, 1, 64, 64, 4, 32, lsq.POLICY_YOKED), (64 * 32, 64 * 8, 64 * 64 * 4, 0, 0)),
     # fp32 state
     (lsq.LsqConfig(1, 2, 64, 32, 32, 1, lsq.POLICY_NONE), (0, 0, 0, 2 * 32 * 64 * 4, 0)),
+    # 16-bit scales: 2 bytes per group
+    (lsq.LsqConfig(2, 3, 128, 128, 4, 32, lsq.POLICY_PERSISTENT, scale_fmt=lsq.SCALE_BF16),
+     (6 * 128 * 64, 6 * 128 * 4 * 2, 0, 0, 0)),
+    (lsq.LsqConfig(1, 1, 64, 64, 8, 16, lsq.POLICY_YOKED, scale_fmt=lsq.SCALE_F16),
+     (64 * 64, 64 * 4 * 2, 64 * 64 * 4, 0, 0)),
     # bypass: a [n][r][Dv] + b [n][2][r][Dk] fp32
     (lsq.LsqConfig(1, 2, 128, 64, 4, 32, lsq.POLICY_PERSISTENT, lrb_rank=4),
      (2 * 64 * 64, 2 * 64 * 16, 0, 0, 2 * 4 * (64 + 2 * 128) * 4)),
@@ -50,6 +55,9 @@ BAD = [
     (dict(group=24), 1), (dict(lrb_rank=9), 1), (dict(lrb_rank=-1), 1),
     (dict(lrb_rank=2, policy=lsq.POLICY_YOKED), 2), (dict(lrb_rank=2, group=16), 2),
     (dict(dk=256, group=32), 2),
+    (dict(scale_fmt=3), 1), (dict(scale_fmt=-1), 1),
+    (dict(bits=32, group=1, policy=lsq.POLICY_NONE, scale_fmt=1), 1),
+    (dict(lrb_rank=2, scale_fmt=2), 2),
 ]
 
 
@@ -157,7 +165,7 @@ def _alloc_all(cfg):
 
 @pytest.mark.parametrize("change", [
     dict(delta=1), dict(policy=lsq.POLICY_YOKED), dict(bits=32, group=1, policy=lsq.POLICY_NONE),
-    dict(dv=32), dict(dv=256), dict(lrb_rank=2),
+    dict(dv=32), dict(dv=256), dict(lrb_rank=2), dict(scale_fmt=2),
 ])
 def test_prefill_rejects_unsupported_handles(change):
     base = dict(batch=1, heads=2, dk=128, dv=128, bits=4, group=32, policy=lsq.POLICY_DYNAMIC)

@@ -102,6 +102,54 @@ def test_group16_matches_oracle(bits, dk, pol, rnd, dc):
     assert rep.excused <= max(2, rep.codes // 20000), str(rep)
 
 
+SF = [(bits, dk, pol, rnd, dl, dc, fmt)
+      for bits in (4, 8)
+      for dk in (128, 64)
+      for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT, lsq.POLICY_YOKED)
+      for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+      for dl in (0, 1)
+      for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)
+      for fmt in (lsq.SCALE_F16, lsq.SCALE_BF16)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc,fmt", SF)
+def test_16bit_scales_match_oracle(bits, dk, pol, rnd, dl, dc, fmt):
+    """binary16 / bfloat16 stored scales: rounded on both sides before the codes
+    are formed; calibration bit-exact, steps to the usual bar."""
+    group = 32 if bits == 4 else 64
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=44, bits=bits, group=min(group, dk),
+                        policy=pol, rounding=rnd, delta=dl, decay=dc, scale_fmt=fmt)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=6, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.excused_groups <= max(2, rep.groups // 100), str(rep)
+
+
+@pytest.mark.parametrize("bits,pol,rnd,fmt", [(b, p, r, f) for b in (4, 8)
+                                              for p in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+                                              for r in (lsq.ROUND_RNE, lsq.ROUND_BDR, lsq.ROUND_DITHER)
+                                              for f in (lsq.SCALE_F16, lsq.SCALE_BF16)])
+def test_group16_16bit_scales_match_oracle(bits, pol, rnd, fmt):
+    """16-element groups with 16-bit scales: both of a lane's scales in one dword."""
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=128, dv=44, bits=bits, group=16, policy=pol,
+                        rounding=rnd, delta=1, decay=lsq.DECAY_DIAG, scale_fmt=fmt)
+    rep = _run_teacher_forced(cfg, steps=5, recipe="gla")
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.excused_groups <= max(2, rep.groups // 100), str(rep)
+
+
+def test_16bit_scale_buffers_are_half_size():
+    for fmt, nbytes in ((lsq.SCALE_F32, 4), (lsq.SCALE_F16, 2), (lsq.SCALE_BF16, 2)):
+        cfg = lsq.LsqConfig(batch=1, heads=2, dk=128, dv=16, bits=4, group=32, scale_fmt=fmt)
+        st = lsq.LsqState(cfg, device=DEV)
+        assert st.scales.element_size() == nbytes
+        assert lsq.lsq_state_sizes(cfg)[1] == 2 * 16 * 4 * nbytes
+
+
 @pytest.mark.parametrize("bits,group", [(4, 64), (4, 128), (8, 32), (8, 128)])
 def test_other_group_sizes(bits, group):
     for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT):
