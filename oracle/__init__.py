@@ -31,6 +31,7 @@ _LIB = os.path.join(_HERE, "liblsq_oracle.so")
 
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
 ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
+ROUND_BDR_A, ROUND_BDR_B = 3, 4        # rejected directional readings (persistent scale only)
 DECAY_SCALAR, DECAY_DIAG = 0, 1
 SCALE_F32, SCALE_F16, SCALE_BF16 = 0, 1, 2
 

@@ -52,7 +52,13 @@ int lsqo_check_config(const lsqo_config* cfg) {
       cfg->policy != LSQO_POLICY_YOKED)
     return -1;
   if (cfg->rounding != LSQO_ROUND_RNE && cfg->rounding != LSQO_ROUND_BDR &&
-      cfg->rounding != LSQO_ROUND_DITHER)
+      cfg->rounding != LSQO_ROUND_DITHER && cfg->rounding != LSQO_ROUND_BDR_A &&
+      cfg->rounding != LSQO_ROUND_BDR_B)
+    return -1;
+  /* the rejected directional readings compare with the stored code, which lies
+   * on this step's grid only under a frozen scale */
+  if ((cfg->rounding == LSQO_ROUND_BDR_A || cfg->rounding == LSQO_ROUND_BDR_B) &&
+      (cfg->policy != LSQO_POLICY_PERSISTENT || cfg->lrb_rank != 0))
     return -1;
   if (cfg->lrb_rank < 0) return -1;
   if (cfg->scale_fmt != LSQO_SCALE_F32 && cfg->scale_fmt != LSQO_SCALE_F16 &&
@@ -254,6 +260,27 @@ static void step_heads(step_job* J) {
             int sigma = sign_f(w) * sign_f(k[c]);
             double yp = (double)sp[c] * (double)inv; /* exact */
             int reversed = (sigma > 0 && c1 < yp) || (sigma < 0 && c1 > yp);
+            if (reversed) {
+              c2 = clampd(c1 + sigma, -qm, qm);
+              if (c2 != c1) J->stats.bdr_fired++;
+            }
+          } else if (cfg->rounding == LSQO_ROUND_BDR_A || cfg->rounding == LSQO_ROUND_BDR_B) {
+            /* The two readings of directional rounding that were not taken,
+             * kept for sensitivity (frozen scale: the stored value C_old s is
+             * code C_old on this step's grid).  A: the update is the total
+             * change from the stored value, sigma = sign(S - C_old s) (the
+             * sign of a rounded double difference is exact).  B': the update
+             * is the rank-one write (sigma as above), the move is measured
+             * from the stored value.  Reversal: c1 on the far side of C_old. */
+            const double cold = (double)C[c];
+            int sigma;
+            if (cfg->rounding == LSQO_ROUND_BDR_A) {
+              const double d = (double)st[c] - cold * (double)snew;
+              sigma = (d > 0.0) - (d < 0.0);
+            } else {
+              sigma = sign_f(w) * sign_f(k[c]);
+            }
+            const int reversed = snew > 0.0f && ((sigma > 0 && c1 < cold) || (sigma < 0 && c1 > cold));
             if (reversed) {
               c2 = clampd(c1 + sigma, -qm, qm);
               if (c2 != c1) J->stats.bdr_fired++;

@@ -86,7 +86,9 @@ extern "C" {
 
 /* enumerations (numeric values mirror the public interface by necessity) */
 enum { LSQO_POLICY_NONE = 0, LSQO_POLICY_DYNAMIC = 1, LSQO_POLICY_PERSISTENT = 2, LSQO_POLICY_YOKED = 3 };
-enum { LSQO_ROUND_RNE = 0, LSQO_ROUND_BDR = 1, LSQO_ROUND_DITHER = 2 };
+enum { LSQO_ROUND_RNE = 0, LSQO_ROUND_BDR = 1, LSQO_ROUND_DITHER = 2,
+       /* rejected directional readings, for sensitivity (persistent only) */
+       LSQO_ROUND_BDR_A = 3, LSQO_ROUND_BDR_B = 4 };
 enum { LSQO_DECAY_SCALAR = 0, LSQO_DECAY_DIAG = 1 };
 enum { LSQO_SCALE_F32 = 0, LSQO_SCALE_F16 = 1, LSQO_SCALE_BF16 = 2 };
 
