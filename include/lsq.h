@@ -42,6 +42,11 @@
  *           c1, u_i = ((i * 0x9E3779B9) mod 2^32 >> 9) * 2^-23 (the Weyl
  *           sequence frac(i (sqrt(5)-1)/2) in fixed point, 23 bits), i =
  *           (t Dv Dk + r Dk + c) mod 2^32 with t the handle's step index
+ *   BDR_A, BDR_B (sensitivity flags; frozen scale s, stored code C_old): the
+ *           readings of "update" and "move" not taken by BDR.  A: sigma_c =
+ *           sign(S_c - C_old s) (exact); B': sigma_c = sign(w) sign(k_c).  If
+ *           (c1 - C_old) * sigma_c < 0 and s > 0 then c = c1 + sigma_c, else c1.
+ *           On a frozen grid A never fires (it equals RNE).
  * with qmax = 2^(bits-1) - 1 (7 for INT4, 127 for INT8).
  *
  * Memory: every pointer below is a DEVICE pointer (row-major, 16-byte
@@ -118,7 +123,16 @@ typedef enum {
   LSQ_POLICY_YOKED = 3
 } lsq_policy;
 
-typedef enum { LSQ_ROUND_RNE = 0, LSQ_ROUND_BDR = 1, LSQ_ROUND_DITHER = 2 } lsq_rounding;
+/* BDR_A and BDR_B are the two readings of directional rounding this library
+ * does not take, for sensitivity runs (persistent scale only, groups of 32 or
+ * more, fp32 scales, no bypass; see the rounding contract above). */
+typedef enum {
+  LSQ_ROUND_RNE = 0,
+  LSQ_ROUND_BDR = 1,
+  LSQ_ROUND_DITHER = 2,
+  LSQ_ROUND_BDR_A = 3,
+  LSQ_ROUND_BDR_B = 4
+} lsq_rounding;
 typedef enum { LSQ_DECAY_SCALAR = 0, LSQ_DECAY_DIAG = 1 } lsq_decay;
 typedef enum { LSQ_SCALE_F32 = 0, LSQ_SCALE_F16 = 1, LSQ_SCALE_BF16 = 2 } lsq_scale_format;
 

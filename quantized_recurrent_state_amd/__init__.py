@@ -16,6 +16,7 @@ from ._lib import LsqError
 
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
 ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
+ROUND_BDR_A, ROUND_BDR_B = 3, 4        # rejected directional readings (sensitivity flags)
 DECAY_SCALAR, DECAY_DIAG = 0, 1
 SCALE_F32, SCALE_F16, SCALE_BF16 = 0, 1, 2
 

@@ -57,8 +57,12 @@ lsq_status check_config(const lsq_config* c) {
   if (c->decay != LSQ_DECAY_SCALAR && c->decay != LSQ_DECAY_DIAG)
     return fail(LSQ_ERR_INVALID_ARG, "decay must be SCALAR or DIAG");
   if (c->rounding != LSQ_ROUND_RNE && c->rounding != LSQ_ROUND_BDR &&
-      c->rounding != LSQ_ROUND_DITHER)
-    return fail(LSQ_ERR_INVALID_ARG, "rounding must be RNE, BDR or DITHER");
+      c->rounding != LSQ_ROUND_DITHER && c->rounding != LSQ_ROUND_BDR_A &&
+      c->rounding != LSQ_ROUND_BDR_B)
+    return fail(LSQ_ERR_INVALID_ARG, "rounding must be RNE, BDR, DITHER, BDR_A or BDR_B");
+  if ((c->rounding == LSQ_ROUND_BDR_A || c->rounding == LSQ_ROUND_BDR_B) &&
+      (c->bits == 32 || c->policy != LSQ_POLICY_PERSISTENT))
+    return fail(LSQ_ERR_INVALID_ARG, "BDR_A and BDR_B compare with the stored code: persistent scale only");
   if (c->bits == 32) {
     if (c->policy != LSQ_POLICY_NONE)
       return fail(LSQ_ERR_INVALID_ARG, "an fp32 state (bits 32) takes policy NONE");
@@ -86,6 +90,11 @@ lsq_status check_config(const lsq_config* c) {
     return fail(LSQ_ERR_INVALID_ARG, "an fp32 state has no scales (scale_fmt F32)");
   if (c->lrb_rank < 0 || c->lrb_rank > 8)
     return fail(LSQ_ERR_INVALID_ARG, "lrb_rank must be 0 to 8");
+  if (c->rounding == LSQ_ROUND_BDR_A || c->rounding == LSQ_ROUND_BDR_B) {
+    if (c->group < 32 || c->scale_fmt != LSQ_SCALE_F32 || c->lrb_rank != 0)
+      return fail(LSQ_ERR_UNSUPPORTED,
+                  "BDR_A and BDR_B run with groups of 32 or more, fp32 scales and no bypass");
+  }
   if (c->lrb_rank > 0) {
     if (c->bits == 32) return fail(LSQ_ERR_INVALID_ARG, "the bypass applies to a quantised state");
     if (c->policy != LSQ_POLICY_DYNAMIC && c->policy != LSQ_POLICY_PERSISTENT)
@@ -180,6 +189,8 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
     e = lsq::launch_lrb_step(a, c.bits, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   } else if (c.bits == 32)
     e = lsq::launch_step_f32(a, c.dk, c.delta, c.decay, stream);
+  else if (c.rounding == LSQ_ROUND_BDR_A || c.rounding == LSQ_ROUND_BDR_B)
+    e = lsq::launch_bdr_alt(a, c.bits, c.dk, c.rounding, c.delta, c.decay, stream);
   else if (c.scale_fmt != LSQ_SCALE_F32)
     e = (c.bits == 4 ? (c.scale_fmt == LSQ_SCALE_F16 ? lsq::launch_step_q4_f16 : lsq::launch_step_q4_bf16)
                      : (c.scale_fmt == LSQ_SCALE_F16 ? lsq::launch_step_q8_f16 : lsq::launch_step_q8_bf16))(

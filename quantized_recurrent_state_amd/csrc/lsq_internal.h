@@ -92,6 +92,8 @@ hipError_t launch_lrb_step(const StepArgs& a, int bits, int dk, int policy, int 
                            int delta, int diag, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int bits, int dk, int dv, int policy, int diag,
                           hipStream_t s);
+hipError_t launch_bdr_alt(const StepArgs& a, int bits, int dk, int rounding, int delta, int diag,
+                          hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace lsq

@@ -21,7 +21,7 @@ import torch
 
 # numeric values of the library's enumerations
 POLICY_NONE, POLICY_DYNAMIC, POLICY_PERSISTENT, POLICY_YOKED = 0, 1, 2, 3
-ROUND_RNE, ROUND_BDR, ROUND_DITHER = 0, 1, 2
+ROUND_RNE, ROUND_BDR, ROUND_DITHER, ROUND_BDR_A, ROUND_BDR_B = 0, 1, 2, 3, 4
 DECAY_SCALAR, DECAY_DIAG = 0, 1
 
 RECIPES = ("la", "gla", "gdn", "mamba2")
@@ -212,6 +212,9 @@ WORKLOADS["stack24-bf16"] = _stack24_variant(
 WORKLOADS["stack24-g16-bf16"] = _stack24_variant(
     "stack24-g16-bf16", "gdn24-512x32-128x128-mixed-int8g64-int4g16-bf16scale-persistent-bdr",
     ROUND_BDR, 16, scale_fmt=2)
+# ... with the directional-rounding reading B' (sensitivity flag)
+WORKLOADS["stack24-bdrb"] = _stack24_variant(
+    "stack24-bdrb", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-bdr-reading-b", ROUND_BDR_B, 32)
 # ... and with a rank-4 Low-Rank Bypass in every layer
 WORKLOADS["stack24-lrb4"] = _stack24_variant(
     "stack24-lrb4", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-bdr-lrb4", ROUND_BDR, 32,

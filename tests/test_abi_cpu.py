@@ -56,6 +56,10 @@ BAD = [
     (dict(lrb_rank=2, policy=lsq.POLICY_YOKED), 2), (dict(lrb_rank=2, group=16), 2),
     (dict(dk=256, group=32), 2),
     (dict(scale_fmt=3), 1), (dict(scale_fmt=-1), 1),
+    (dict(rounding=5), 1), (dict(rounding=3, policy=lsq.POLICY_DYNAMIC), 1),
+    (dict(rounding=4, policy=lsq.POLICY_YOKED), 1),
+    (dict(rounding=4, policy=lsq.POLICY_PERSISTENT, group=16), 2),
+    (dict(rounding=3, policy=lsq.POLICY_PERSISTENT, scale_fmt=2), 2),
     (dict(bits=32, group=1, policy=lsq.POLICY_NONE, scale_fmt=1), 1),
     (dict(lrb_rank=2, scale_fmt=2), 2),
 ]

@@ -142,6 +142,29 @@ def test_group16_16bit_scales_match_oracle(bits, pol, rnd, fmt):
     assert rep.excused_groups <= max(2, rep.groups // 100), str(rep)
 
 
+ALT = [(bits, dk, rnd, dl, dc)
+       for bits in (4, 8)
+       for dk in (128, 64)
+       for rnd in (lsq.ROUND_BDR_A, lsq.ROUND_BDR_B)
+       for dl in (0, 1)
+       for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,rnd,dl,dc", ALT)
+def test_rejected_bdr_readings_match_oracle(bits, dk, rnd, dl, dc):
+    """The two directional readings not taken (sensitivity flags), persistent scale."""
+    group = 32 if bits == 4 else 64
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=44, bits=bits, group=min(group, dk),
+                        policy=lsq.POLICY_PERSISTENT, rounding=rnd, delta=dl, decay=dc)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=6, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    if rnd == lsq.ROUND_BDR_A:
+        assert rep.bdr_fired == 0                     # equals RNE on a frozen grid
+
+
 def test_16bit_scale_buffers_are_half_size():
     for fmt, nbytes in ((lsq.SCALE_F32, 4), (lsq.SCALE_F16, 2), (lsq.SCALE_BF16, 2)):
         cfg = lsq.LsqConfig(batch=1, heads=2, dk=128, dv=16, bits=4, group=32, scale_fmt=fmt)
