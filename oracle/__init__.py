@@ -122,7 +122,7 @@ class OracleConfig:
 
     @property
     def ngroups(self) -> int:
-        return self.dk // self.group
+        return self.dk // self.group if self.group else 1
 
     def c(self) -> _Config:
         return _Config(**asdict(self))
@@ -163,7 +163,8 @@ def zero_state(cfg: OracleConfig) -> OracleState:
     if cfg.bits == 32:
         return OracleState(f32=np.zeros((n, cfg.dv, cfg.dk), np.float32))
     st = OracleState(codes=np.zeros((n, cfg.dv, cfg.dk), np.int8),
-                     scales=np.zeros((n, cfg.dv, cfg.ngroups), np.float32))
+                     scales=np.zeros((n, cfg.dv, cfg.ngroups) if cfg.group else (n, 1, 1),
+                                     np.float32))
     if cfg.policy == POLICY_YOKED:
         st.ref = np.zeros((n, cfg.dv, cfg.dk), np.float32)
     if cfg.lrb_rank > 0:

@@ -46,7 +46,14 @@ int lsqo_check_config(const lsqo_config* cfg) {
   if (cfg->decay != LSQO_DECAY_SCALAR && cfg->decay != LSQO_DECAY_DIAG) return -1;
   if (cfg->bits == 32) return (cfg->policy == LSQO_POLICY_NONE && cfg->scale_fmt == 0) ? 0 : -1;
   if (cfg->bits != 4 && cfg->bits != 8) return -1;
-  if (cfg->group <= 0 || cfg->dk % cfg->group != 0) return -1;
+  if (cfg->group == 0) {
+    /* one scale per head: dynamic or persistent, RNE or BDR, no bypass */
+    if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT) return -1;
+    if (cfg->rounding != LSQO_ROUND_RNE && cfg->rounding != LSQO_ROUND_BDR) return -1;
+    if (cfg->lrb_rank != 0) return -1;
+  } else if (cfg->group < 0 || cfg->dk % cfg->group != 0) {
+    return -1;
+  }
   if (cfg->bits == 4 && cfg->dk % 2 != 0) return -1;
   if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT &&
       cfg->policy != LSQO_POLICY_YOKED)
@@ -165,6 +172,78 @@ typedef struct {
   lsqo_stats stats;
 } step_job;
 
+/* One head whose state has a single scale (group == 0, the per-head
+ * granularity): every row is updated first and S_t kept whole; the scale is
+ * taken over all of S_t (dynamic: fl(absmax/qmax) rounded to the stored
+ * format) or kept (persistent); then every element is requantised as in the
+ * group case, with directional rounding measured from S' as there. */
+static void step_head_scale(step_job* J, int64_t h, const float* q, const float* k,
+                            const float* v, const float* alpha, float beta) {
+  const lsqo_config* cfg = J->cfg;
+  const int dk = cfg->dk, dv = cfg->dv, qm = qmax_of(cfg->bits);
+  const int diag = cfg->decay == LSQO_DECAY_DIAG;
+  int8_t* C = J->codes + h * (int64_t)dv * dk;
+  float* s = J->scales + h;
+  float* SP = (float*)malloc(sizeof(float) * (size_t)dv * dk);
+  float* ST = (float*)malloc(sizeof(float) * (size_t)dv * dk);
+  float* W = (float*)malloc(sizeof(float) * (size_t)dv);
+  float amax = 0.0f;
+  for (int r = 0; r < dv; ++r) {
+    float* sp = SP + (int64_t)r * dk;
+    float* st = ST + (int64_t)r * dk;
+    for (int c = 0; c < dk; ++c) {
+      const float m = s[0] * (diag ? alpha[c] : alpha[0]);
+      sp[c] = (float)C[(int64_t)r * dk + c] * m;
+    }
+    float u = 0.0f;
+    if (cfg->delta) {
+      double acc = 0.0;
+      for (int c = 0; c < dk; ++c) acc += (double)sp[c] * (double)k[c];
+      u = (float)acc;
+    }
+    const float w = beta * (v[r] - u);
+    W[r] = w;
+    double o = 0.0;
+    for (int c = 0; c < dk; ++c) {
+      st[c] = fmaf(w, k[c], sp[c]);
+      o += (double)st[c] * (double)q[c];
+      const float a = fabsf(st[c]);
+      if (a > amax) amax = a;
+    }
+    J->o[h * dv + r] = (float)o;
+  }
+  const float snew = (cfg->policy == LSQO_POLICY_PERSISTENT)
+                         ? s[0] : scale_as_stored(amax / (float)qm, cfg->scale_fmt);
+  const float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
+  for (int r = 0; r < dv; ++r) {
+    for (int c = 0; c < dk; ++c) {
+      const int64_t i = (int64_t)r * dk + c;
+      const double y = (double)ST[i] * (double)inv;    /* exact */
+      const double yp = (double)SP[i] * (double)inv;   /* exact */
+      if (J->y_out) {
+        J->y_out[h * (int64_t)dv * dk + i] = y;
+        J->yp_out[h * (int64_t)dv * dk + i] = yp;
+      }
+      const double c0 = round_half_even(y);
+      const double c1 = clampd(c0, -qm, qm);
+      if (c1 != c0) J->stats.clamped++;
+      double c2 = c1;
+      if (cfg->rounding == LSQO_ROUND_BDR) {
+        const int sigma = sign_f(W[r]) * sign_f(k[c]);
+        if ((sigma > 0 && c1 < yp) || (sigma < 0 && c1 > yp)) {
+          c2 = clampd(c1 + sigma, -qm, qm);
+          if (c2 != c1) J->stats.bdr_fired++;
+        }
+      }
+      C[i] = (int8_t)c2;
+    }
+  }
+  s[0] = snew;
+  free(SP);
+  free(ST);
+  free(W);
+}
+
 static void step_heads(step_job* J) {
   const lsqo_config* cfg = J->cfg;
   const int dk = cfg->dk, dv = cfg->dv;
@@ -187,6 +266,10 @@ static void step_heads(step_job* J) {
       continue;
     }
 
+    if (cfg->group == 0) {
+      step_head_scale(J, h, q, k, v, alpha, beta);
+      continue;
+    }
     const int g = cfg->group, ng = dk / g;
     const int qm = qmax_of(cfg->bits);
     for (int r = 0; r < dv; ++r) {
@@ -556,7 +639,9 @@ static float quantise_block_i8(const float* x, int64_t n, int8_t* q) {
 
 int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes, float* scales,
                  const float* k, const float* v, const float* alpha, const float* beta) {
-  if (lsqo_check_config(cfg) || cfg->bits == 32 || cfg->delta != 0 || T < 0 || chunk < 1) return -1;
+  if (lsqo_check_config(cfg) || cfg->bits == 32 || cfg->delta != 0 || T < 0 || chunk < 1 ||
+      cfg->group == 0)
+    return -1;
   if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT) return -1;
   const int dk = cfg->dk, dv = cfg->dv, g = cfg->group, ng = dk / g, qm = qmax_of(cfg->bits);
   const int diag = cfg->decay == LSQO_DECAY_DIAG;
@@ -640,6 +725,24 @@ int lsqo_calibrate(const lsqo_config* cfg, const float* S, int8_t* codes, float*
     memcpy(f32, S, sizeof(float) * (size_t)(rows * dk));
     return 0;
   }
+  if (cfg->group == 0) {                      /* one scale per head */
+    const int64_t per = (int64_t)cfg->dv * dk;
+    const int qmh = qmax_of(cfg->bits);
+    for (int64_t h = 0; h < n; ++h) {
+      const float* x = S + h * per;
+      float amax = 0.0f;
+      for (int64_t i = 0; i < per; ++i) {
+        const float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+      }
+      const float s = scale_as_stored(amax / (float)qmh, cfg->scale_fmt);
+      const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+      for (int64_t i = 0; i < per; ++i)
+        codes[h * per + i] = (int8_t)clampd(round_half_even((double)x[i] * (double)inv), -qmh, qmh);
+      scales[h] = s;
+    }
+    return 0;
+  }
   const int g = cfg->group, ng = dk / g, qm = qmax_of(cfg->bits);
   for (int64_t r = 0; r < rows; ++r) {
     const float* x = S + r * dk;
@@ -665,7 +768,13 @@ int lsqo_calibrate(const lsqo_config* cfg, const float* S, int8_t* codes, float*
 int lsqo_dequantize(const lsqo_config* cfg, const int8_t* codes, const float* scales, float* out) {
   if (lsqo_check_config(cfg) || cfg->bits == 32) return -1;
   const int64_t rows = (int64_t)cfg->batch * cfg->heads * cfg->dv;
-  const int dk = cfg->dk, g = cfg->group, ng = dk / g;
+  const int dk = cfg->dk;
+  if (cfg->group == 0) {                      /* one scale per head */
+    for (int64_t r = 0; r < rows; ++r)
+      for (int c = 0; c < dk; ++c) out[r * dk + c] = (float)codes[r * dk + c] * scales[r / cfg->dv];
+    return 0;
+  }
+  const int g = cfg->group, ng = dk / g;
   for (int64_t r = 0; r < rows; ++r)
     for (int c = 0; c < dk; ++c) out[r * dk + c] = (float)codes[r * dk + c] * scales[r * ng + c / g];
   return 0;

@@ -95,7 +95,9 @@ enum { LSQO_SCALE_F32 = 0, LSQO_SCALE_F16 = 1, LSQO_SCALE_BF16 = 2 };
 typedef struct {
   int32_t batch, heads, dk, dv;
   int32_t bits;     /* 4, 8, or 32 (unquantised fp32 state) */
-  int32_t group;    /* group size along Dk (ignored for bits == 32) */
+  int32_t group;    /* group size along Dk (ignored for bits == 32); 0: one scale
+                       per head (dynamic or persistent, RNE or BDR, no bypass,
+                       no prefill; scales then hold [heads] values) */
   int32_t policy;   /* LSQO_POLICY_* */
   int32_t rounding; /* LSQO_ROUND_* */
   int32_t delta;    /* 0: linear write, 1: delta-rule correction */
