@@ -62,7 +62,8 @@
  *          most negative code (-8, -128) is never produced and is not a
  *          valid input.
  *   scales [heads][Dv][Dk/group], one per contiguous group along Dk: fp32,
- *          or (scale_fmt) IEEE binary16 or bfloat16 bit patterns, 2 bytes.
+ *          or (scale_fmt) IEEE binary16 or bfloat16 bit patterns, 2 bytes;
+ *          group = 0: [heads] fp32, one per head.
  *   ref    [heads][Dv][Dk] fp32, the yoked policy's reference state.
  *   f32    [heads][Dv][Dk] fp32, the state of the unquantised mode (bits 32).
  *   lrb    Low-Rank Bypass buffer (lrb_rank = r > 0), fp32: a [heads][r][Dv]
@@ -141,7 +142,12 @@ typedef enum { LSQ_SCALE_F32 = 0, LSQ_SCALE_F16 = 1, LSQ_SCALE_BF16 = 2 } lsq_sc
  *   group  group size along Dk; must divide dk.  This build supports
  *          power-of-two groups of 16 to Dk elements (one lane owns 32
  *          consecutive elements of a row: one group, part of one, or two
- *          16-element groups) and Dk in {64, 128}.  INT4 with 16-element
+ *          16-element groups) and Dk in {64, 128}.  group = Dk is one scale
+ *          per row.  group = 0 is one scale per head for the whole Dv x Dk
+ *          state (scales [heads] fp32): DYNAMIC (the absmax over every
+ *          element after the step's update, so all rows are updated before
+ *          any is requantised) or PERSISTENT (calibrated over the head), RNE
+ *          or BDR, fp32 scale, no bypass, no prefill, Dv <= 1024.  INT4 with 16-element
  *          groups and fp32 scales stores 6 bits per element, 5.33x less
  *          than an fp32 state.
  *   delta  0: linear write, 1: delta-rule correction

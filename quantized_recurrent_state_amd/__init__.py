@@ -152,7 +152,8 @@ class LsqState:
                                      device=self.device)
             sdt = {SCALE_F32: torch.float32, SCALE_F16: torch.float16,
                    SCALE_BF16: torch.bfloat16}[cfg.scale_fmt]
-            self.scales = torch.empty((n, dv, dk // cfg.group), dtype=sdt, device=self.device)
+            sshape = (n, dv, dk // cfg.group) if cfg.group else (n, 1, 1)   # group 0: per head
+            self.scales = torch.empty(sshape, dtype=sdt, device=self.device)
         if n_ref:
             self.ref = torch.empty((n, dv, dk), dtype=torch.float32, device=self.device)
         if cfg.bits == 32:

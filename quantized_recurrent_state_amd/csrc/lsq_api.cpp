@@ -70,13 +70,21 @@ lsq_status check_config(const lsq_config* c) {
     if (c->policy != LSQ_POLICY_DYNAMIC && c->policy != LSQ_POLICY_PERSISTENT &&
         c->policy != LSQ_POLICY_YOKED)
       return fail(LSQ_ERR_INVALID_ARG, "a quantised state takes policy DYNAMIC, PERSISTENT or YOKED");
-    if (c->group <= 0 || c->dk % c->group != 0)
-      return fail(LSQ_ERR_INVALID_ARG, "group must be positive and divide dk");
+    if (c->group < 0 || (c->group > 0 && c->dk % c->group != 0))
+      return fail(LSQ_ERR_INVALID_ARG, "group must be 0 (one scale per head) or divide dk");
+    if (c->group == 0 && (c->policy == LSQ_POLICY_YOKED || c->rounding == LSQ_ROUND_DITHER ||
+                          c->rounding == LSQ_ROUND_BDR_A || c->rounding == LSQ_ROUND_BDR_B))
+      return fail(LSQ_ERR_INVALID_ARG,
+                  "one scale per head takes the DYNAMIC or PERSISTENT policy, RNE or BDR");
   } else {
     return fail(LSQ_ERR_INVALID_ARG, "bits must be 4, 8 or 32");
   }
   if (c->dk != 64 && c->dk != 128) return fail(LSQ_ERR_UNSUPPORTED, "dk %d: this build has dk 64 and 128", c->dk);
-  if (c->bits != 32) {
+  if (c->bits != 32 && c->group == 0) {
+    if (c->scale_fmt != LSQ_SCALE_F32 || c->lrb_rank != 0)
+      return fail(LSQ_ERR_UNSUPPORTED, "one scale per head runs with an fp32 scale and no bypass");
+    if (c->dv > 1024) return fail(LSQ_ERR_UNSUPPORTED, "one scale per head needs dv <= 1024");
+  } else if (c->bits != 32) {
     constexpr int min_group = 16;   // a lane owns 32 elements: one group, or two of 16
     if (c->group < min_group || (c->group & (c->group - 1)) != 0)
       return fail(LSQ_ERR_UNSUPPORTED,
@@ -121,7 +129,9 @@ void sizes_of(const lsq_config& c, size_t (&sz)[kBuffers]) {
     return;
   }
   sz[0] = elems * c.bits / 8;
-  sz[1] = (size_t)n_heads(c) * c.dv * (c.dk / c.group) * (c.scale_fmt == LSQ_SCALE_F32 ? 4 : 2);
+  sz[1] = (c.group == 0) ? (size_t)n_heads(c) * 4     // one fp32 scale per head
+                         : (size_t)n_heads(c) * c.dv * (c.dk / c.group) *
+                               (c.scale_fmt == LSQ_SCALE_F32 ? 4 : 2);
   if (c.policy == LSQ_POLICY_YOKED) sz[2] = elems * 4;
   if (c.lrb_rank > 0) sz[4] = (size_t)n_heads(c) * c.lrb_rank * (c.dv + 2 * (size_t)c.dk) * 4;
 }
@@ -171,7 +181,13 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
   a.n_heads = (int32_t)n_heads(c);
   a.dv = c.dv;
   a.group = c.group;
-  a.ng = (c.bits == 32) ? 0 : c.dk / c.group;
+  a.ng = (c.bits == 32 || c.group == 0) ? 0 : c.dk / c.group;
+  if (c.bits != 32 && c.group == 0 && c.policy == LSQ_POLICY_PERSISTENT) {
+    // a frozen head scale: the main step kernel with row groups of Dk whose
+    // scale address does not move with the row
+    a.group = c.dk;
+    a.head_scale = 1;
+  }
   choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves);
   constexpr uint32_t kWeyl = 0x9E3779B9u;   // 2^32 (sqrt(5)-1)/2, truncated
   a.dither_base = (uint32_t)((uint64_t)st->step * (uint64_t)c.dv * (uint64_t)c.dk) * kWeyl;
@@ -189,6 +205,8 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
     e = lsq::launch_lrb_step(a, c.bits, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   } else if (c.bits == 32)
     e = lsq::launch_step_f32(a, c.dk, c.delta, c.decay, stream);
+  else if (c.group == 0 && c.policy == LSQ_POLICY_DYNAMIC)
+    e = lsq::launch_head_scale(a, c.bits, c.dk, c.policy, c.rounding, c.delta, c.decay, stream);
   else if (c.rounding == LSQ_ROUND_BDR_A || c.rounding == LSQ_ROUND_BDR_B)
     e = lsq::launch_bdr_alt(a, c.bits, c.dk, c.rounding, c.delta, c.decay, stream);
   else if (c.scale_fmt != LSQ_SCALE_F32)
@@ -304,6 +322,12 @@ lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream) {
   a.n_heads = (int32_t)n_heads(c);
   a.dv = c.dv;
   a.group = c.group;
+  if (c.group == 0) {                  // one scale per head
+    a.ng = 0;
+    lsq_status s = hip_status(lsq::launch_calibrate_head(a, c.bits, c.dk, hs), "calibrate launch");
+    if (s == LSQ_OK) st->calibrated = 1;
+    return s;
+  }
   a.ng = c.dk / c.group;
   choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves);
   lsq_status s = hip_status(lsq::launch_calibrate(a, c.bits, c.dk, hs), "calibrate launch");
@@ -384,6 +408,7 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
   if (c.scale_fmt != LSQ_SCALE_F32) return fail(LSQ_ERR_UNSUPPORTED, "prefill keeps fp32 scales");
   if (c.dv != 64 && c.dv != 128)
     return fail(LSQ_ERR_UNSUPPORTED, "dv %d: prefill has dv 64 and 128", c.dv);
+  if (c.group == 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill needs group scales along Dk");
   if (c.dk / c.group > 8) return fail(LSQ_ERR_UNSUPPORTED, "prefill holds at most 8 groups per row");
   if (c.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
     return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");

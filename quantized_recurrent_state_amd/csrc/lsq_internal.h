@@ -39,6 +39,7 @@ struct StepArgs {
   int32_t lrb_merge;     // 1 when this step fills the last slot and merges
   int32_t lrb_cin, lrb_cout;  // b copy read / written this step
   int32_t sfmt;          // stored scale format: 0 fp32, 1 binary16, 2 bfloat16
+  int32_t head_scale;    // 1: one scale per head (scales [n]), broadcast to every row
 };
 
 // Arguments of a calibration launch: quantise an fp32 state into codes/scales.
@@ -94,6 +95,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int bits, int dk, int dv, int po
                           hipStream_t s);
 hipError_t launch_bdr_alt(const StepArgs& a, int bits, int dk, int rounding, int delta, int diag,
                           hipStream_t s);
+hipError_t launch_head_scale(const StepArgs& a, int bits, int dk, int policy, int rounding,
+                             int delta, int diag, hipStream_t s);
+hipError_t launch_calibrate_head(const CalibArgs& a, int bits, int dk, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace lsq

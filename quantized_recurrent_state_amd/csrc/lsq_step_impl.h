@@ -868,6 +868,7 @@ void step_kernel(StepArgs a) {
     L.H.codes = a.codes + row0 * (DK * BITS / 8);
     L.H.scales = reinterpret_cast<float*>(reinterpret_cast<char*>(a.scales) +
                                           row0 * a.ng * (SF ? 2 : 4));
+    if (a.head_scale) L.H.scales = a.scales + L.h;   // one frozen scale per head (ng = 0)
     L.H.v = a.v + row0;
     L.H.o = a.o + row0;
     L.H.o_ref = a.o_ref ? a.o_ref + row0 : nullptr;

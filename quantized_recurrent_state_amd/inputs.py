@@ -185,14 +185,15 @@ WORKLOADS = {
 
 
 def _stack24_variant(key: str, name: str, rounding: int, int4_group: int,
-                     lrb_rank: int = 0, scale_fmt: int = 0) -> Workload:
+                     lrb_rank: int = 0, scale_fmt: int = 0, int8_group: int = 64) -> Workload:
     base = WORKLOADS["stack24"]
+    gname = lambda g: f"g{g}" if g else "head"       # group 0: one scale per head
     return Workload(name, base.recipe, base.batch, base.heads, base.dk, base.dv, base.delta,
                     base.decay, base.steps, base.warmup,
-                    (Arm("layers0-3-int8g64", 8, 64, POLICY_PERSISTENT, rounding, tuple(range(0, 4)),
-                         lrb_rank, scale_fmt),
-                     Arm(f"layers4-23-int4g{int4_group}", 4, int4_group, POLICY_PERSISTENT, rounding,
-                         tuple(range(4, 24)), lrb_rank, scale_fmt)),
+                    (Arm(f"layers0-3-int8{gname(int8_group)}", 8, int8_group, POLICY_PERSISTENT,
+                         rounding, tuple(range(0, 4)), lrb_rank, scale_fmt),
+                     Arm(f"layers4-23-int4{gname(int4_group)}", 4, int4_group, POLICY_PERSISTENT,
+                         rounding, tuple(range(4, 24)), lrb_rank, scale_fmt)),
                     shared_inputs=False)
 
 
@@ -212,6 +213,15 @@ WORKLOADS["stack24-bf16"] = _stack24_variant(
 WORKLOADS["stack24-g16-bf16"] = _stack24_variant(
     "stack24-g16-bf16", "gdn24-512x32-128x128-mixed-int8g64-int4g16-bf16scale-persistent-bdr",
     ROUND_BDR, 16, scale_fmt=2)
+# Gated DeltaNet with a dynamic scale per head (group 0): every row updated before any is
+# requantised (two passes over the head's rows)
+WORKLOADS["gdn-head"] = Workload("gdn-256x16-128x128-int4-headscale-dynamic", "gdn", 256, 16, 128, 128,
+                                 1, DECAY_SCALAR, 2048, 0,
+                                 (Arm("int4head-dynamic", 4, 0, POLICY_DYNAMIC, ROUND_RNE),))
+# ... with one scale per head (group 0) instead of group scales
+WORKLOADS["stack24-head"] = _stack24_variant(
+    "stack24-head", "gdn24-512x32-128x128-mixed-int8-int4-headscale-persistent-bdr", ROUND_BDR, 0,
+    int8_group=0)
 # ... with the directional-rounding reading B' (sensitivity flag)
 WORKLOADS["stack24-bdrb"] = _stack24_variant(
     "stack24-bdrb", "gdn24-512x32-128x128-mixed-int8g64-int4g32-persistent-bdr-reading-b", ROUND_BDR_B, 32)

@@ -65,7 +65,8 @@ def algorithmic_bytes(cfg: LsqConfig, with_o_ref: bool = False) -> int:
     else:
         state = 2 * dv * dk * cfg.bits // 8
         sbytes = 4 if cfg.scale_fmt == 0 else 2
-        state += dv * (dk // cfg.group) * sbytes * (2 if cfg.policy in (POLICY_DYNAMIC, POLICY_YOKED) else 1)
+        nscale = dv * (dk // cfg.group) if cfg.group else 1     # group 0: one scale per head
+        state += nscale * sbytes * (2 if cfg.policy in (POLICY_DYNAMIC, POLICY_YOKED) else 1)
         if cfg.policy == POLICY_YOKED:
             state += 2 * 4 * dv * dk
     ins = 4 * (2 * dk + dv + (dk if cfg.decay == DECAY_DIAG else 1) + 1)

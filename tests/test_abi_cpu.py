@@ -39,6 +39,8 @@ def test_every_declared_symbol_is_exported():
      (6 * 128 * 64, 6 * 128 * 4 * 2, 0, 0, 0)),
     (lsq.LsqConfig(1, 1, 64, 64, 8, 16, lsq.POLICY_YOKED, scale_fmt=lsq.SCALE_F16),
      (64 * 64, 64 * 4 * 2, 64 * 64 * 4, 0, 0)),
+    # one fp32 scale per head
+    (lsq.LsqConfig(2, 3, 128, 128, 4, 0, lsq.POLICY_DYNAMIC), (6 * 128 * 64, 6 * 4, 0, 0, 0)),
     # bypass: a [n][r][Dv] + b [n][2][r][Dk] fp32
     (lsq.LsqConfig(1, 2, 128, 64, 4, 32, lsq.POLICY_PERSISTENT, lrb_rank=4),
      (2 * 64 * 64, 2 * 64 * 16, 0, 0, 2 * 4 * (64 + 2 * 128) * 4)),
@@ -49,7 +51,7 @@ def test_state_sizes(cfg, want):
 
 BAD = [
     (dict(bits=5), 1), (dict(bits=32, policy=lsq.POLICY_DYNAMIC), 1),
-    (dict(policy=lsq.POLICY_NONE), 1), (dict(group=48), 1), (dict(group=0), 1),
+    (dict(policy=lsq.POLICY_NONE), 1), (dict(group=48), 1),
     (dict(delta=2), 1), (dict(decay=3), 1), (dict(rounding=7), 1), (dict(batch=-1), 1),
     (dict(dk=96, group=32), 2), (dict(group=8), 2), (dict(bits=8, group=8), 2),
     (dict(group=24), 1), (dict(lrb_rank=9), 1), (dict(lrb_rank=-1), 1),
@@ -57,6 +59,9 @@ BAD = [
     (dict(dk=256, group=32), 2),
     (dict(scale_fmt=3), 1), (dict(scale_fmt=-1), 1),
     (dict(rounding=5), 1), (dict(rounding=3, policy=lsq.POLICY_DYNAMIC), 1),
+    (dict(group=-1), 1), (dict(group=0, policy=lsq.POLICY_YOKED), 1),
+    (dict(group=0, rounding=2), 1), (dict(group=0, scale_fmt=2), 2),
+    (dict(group=0, lrb_rank=2), 2), (dict(group=0, dv=1025), 2),
     (dict(rounding=4, policy=lsq.POLICY_YOKED), 1),
     (dict(rounding=4, policy=lsq.POLICY_PERSISTENT, group=16), 2),
     (dict(rounding=3, policy=lsq.POLICY_PERSISTENT, scale_fmt=2), 2),
@@ -169,7 +174,7 @@ def _alloc_all(cfg):
 
 @pytest.mark.parametrize("change", [
     dict(delta=1), dict(policy=lsq.POLICY_YOKED), dict(bits=32, group=1, policy=lsq.POLICY_NONE),
-    dict(dv=32), dict(dv=256), dict(lrb_rank=2), dict(scale_fmt=2),
+    dict(dv=32), dict(dv=256), dict(lrb_rank=2), dict(scale_fmt=2), dict(group=0),
 ])
 def test_prefill_rejects_unsupported_handles(change):
     base = dict(batch=1, heads=2, dk=128, dv=128, bits=4, group=32, policy=lsq.POLICY_DYNAMIC)

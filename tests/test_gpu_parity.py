@@ -165,6 +165,27 @@ def test_rejected_bdr_readings_match_oracle(bits, dk, rnd, dl, dc):
         assert rep.bdr_fired == 0                     # equals RNE on a frozen grid
 
 
+HEAD = [(bits, dk, pol, rnd, dl, dc)
+        for bits in (4, 8)
+        for dk in (128, 64)
+        for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+        for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+        for dl in (0, 1)
+        for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc", HEAD)
+def test_head_scale_matches_oracle(bits, dk, pol, rnd, dl, dc):
+    """One scale per head (group 0): two passes over the head's rows."""
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=100, bits=bits, group=0, policy=pol,
+                        rounding=rnd, delta=dl, decay=dc)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=6, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
 def test_16bit_scale_buffers_are_half_size():
     for fmt, nbytes in ((lsq.SCALE_F32, 4), (lsq.SCALE_F16, 2), (lsq.SCALE_BF16, 2)):
         cfg = lsq.LsqConfig(batch=1, heads=2, dk=128, dv=16, bits=4, group=32, scale_fmt=fmt)
