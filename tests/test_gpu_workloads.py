@@ -10,7 +10,10 @@ inputs), on sampled heads compared teacher-forced with the CPU oracle.
   mamba2   8192 heads, Dv 64, INT8 g64 persistent, BDR vs RNE: 4096 steps,
            checked at sampled steps
   stack24  393216 heads in two launches (INT8 g64 layers 0-3, INT4 g32 layers
-           4-23), persistent, BDR: warmup, calibration and the first steps
+           4-23), persistent, BDR: warmup, calibration and the first steps; the
+           same for the stack's variants the benchmark runs (RNE, Weyl dither,
+           16-element groups, bfloat16 scales, one scale per head, reading B'),
+           and for Gated DeltaNet with a dynamic scale per head
 """
 import numpy as np
 import pytest
@@ -64,6 +67,7 @@ def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64):
                 chk = t in check_steps
                 if chk:
                     before = snapshot(st, heads=sels[ai])
+                    step_index = st.step_index          # the dither's sequence position
                 out = st.step(d["q"][j], d["k"][j], d["v"][j], d["alpha"][j], d["beta"][j])
                 if chk:
                     o, o_ref = out if st.cfg.policy == lsq.POLICY_YOKED else (out, None)
@@ -71,7 +75,7 @@ def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64):
                     after = snapshot(st, heads=sel)
                     inp = tuple(d[x][j].index_select(0, sel).cpu().numpy()
                                 for x in ("q", "k", "v", "alpha", "beta"))
-                    ocfg = ocfg_of(st.cfg).replace(batch=len(sel), heads=1)
+                    ocfg = ocfg_of(st.cfg, step=step_index).replace(batch=len(sel), heads=1)
                     reps[ai].add(compare_step(
                         ocfg, before, inp, after, o.index_select(0, sel).cpu().numpy(),
                         None if o_ref is None else o_ref.index_select(0, sel).cpu().numpy()))
@@ -131,8 +135,13 @@ def test_mamba2_bdr_vs_rne():
     assert reps[0].bdr_fired > 0 and reps[1].bdr_fired == 0
 
 
-def test_stack24_full_size_first_steps():
-    wl = WORKLOADS["stack24"]
+@pytest.mark.parametrize("key", ["stack24", "stack24-rne", "stack24-dither", "stack24-g16",
+                                 "stack24-bf16", "stack24-g16-bf16", "stack24-head", "stack24-bdrb",
+                                 "gdn-head"])
+def test_full_size_first_steps(key):
+    wl = WORKLOADS[key]
     states, t0 = _prepare(wl, sel_n=48)
     reps = _run_checked(wl, states, t0, 6, set(range(6)), sel_n=48, chunk=6)
     _assert_ok(wl, reps)
+    del states
+    torch.cuda.empty_cache()
