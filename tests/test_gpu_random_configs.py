@@ -1,0 +1,55 @@
+"""Seeded random sweep of configurations against the oracle (teacher-forced).
+
+Draws bits, Dk, Dv (1 to 200, ragged against the rows a wave covers), heads,
+group (16 to Dk, or one per head), scale policy, rounding (RNE, BDR, dither,
+the two rejected readings), delta rule, decay and scale format, repaired into
+combinations the library runs (a configuration it refuses is skipped on its
+own status code); each runs a few steps against the oracle to the decode bar.
+The bypass has its own harness (slots compared every step).
+"""
+import numpy as np
+import pytest
+
+import quantized_recurrent_state_amd as lsq
+from tests.test_gpu_parity import _run_teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    """A random configuration, repaired into a combination the library runs."""
+    rng = np.random.default_rng(1000 + seed)
+    bits = int(rng.choice([4, 8]))
+    dk = int(rng.choice([64, 128]))
+    dv = int(rng.integers(1, 201))
+    group = int(rng.choice([0, 16, 32, 64, dk]))
+    policy = int(rng.choice([lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT, lsq.POLICY_YOKED]))
+    rounding = int(rng.choice([lsq.ROUND_RNE, lsq.ROUND_BDR, lsq.ROUND_DITHER, lsq.ROUND_BDR_A,
+                               lsq.ROUND_BDR_B]))
+    scale_fmt = int(rng.choice([0, 0, 1, 2]))
+    if rounding in (lsq.ROUND_BDR_A, lsq.ROUND_BDR_B):   # stored-code readings: frozen scale
+        policy, group, scale_fmt = lsq.POLICY_PERSISTENT, max(group, 32), 0
+    if group == 0:                                       # one scale per head
+        policy = min(policy, lsq.POLICY_PERSISTENT)
+        rounding = rounding if rounding in (lsq.ROUND_RNE, lsq.ROUND_BDR) else lsq.ROUND_BDR
+        scale_fmt = 0
+    return lsq.LsqConfig(batch=int(rng.integers(1, 3)), heads=int(rng.integers(1, 4)), dk=dk, dv=dv,
+                         bits=bits, group=group, policy=policy, rounding=rounding,
+                         delta=int(rng.integers(0, 2)), decay=int(rng.integers(0, 2)),
+                         scale_fmt=scale_fmt)
+
+
+@pytest.mark.parametrize("seed", range(80))
+def test_random_configuration(seed):
+    cfg = _draw(seed)
+    try:
+        lsq.lsq_state_sizes(cfg)
+    except lsq.LsqError as e:
+        assert e.status in (1, 2)
+        pytest.skip(f"not supported: {cfg}")
+    recipe = "gla" if cfg.decay == lsq.DECAY_DIAG else ("gdn" if cfg.delta else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=4, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.excused_groups <= max(2, rep.groups // 100), str(rep)
