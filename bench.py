@@ -124,20 +124,26 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, events around every launch of the dominant kernel
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    # events around every launch of every arm, on the launch stream
+    ev_s = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in arms]
+    ev_e = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in arms]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j, t in enumerate(range(W, W + K)):
         for i, a in enumerate(arms):
-            if i == dom:
-                ev_s[j].record(stream)
+            ev_s[i][j].record(stream)
             launch(a, t)
-            if i == dom:
-                ev_e[j].record(stream)
+            ev_e[i][j].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in zip(ev_s, ev_e)]
+    for i, a in enumerate(arms):
+        ms = sorted(x.elapsed_time(y) for x, y in zip(ev_s[i], ev_e[i]))
+        a["launch_us"] = {"median": round(ms[len(ms) // 2] * 1e3, 2),
+                          "p10": round(ms[len(ms) // 10] * 1e3, 2),
+                          "p90": round(ms[(9 * len(ms)) // 10] * 1e3, 2),
+                          "mean": round(sum(ms) / len(ms) * 1e3, 2)}
+        a["kernel_gbs"] = round(a["bytes"] / (sum(ms) / len(ms) * 1e-3) / 1e9, 2)
+    kern_ms = [x.elapsed_time(y) for x, y in zip(ev_s[dom], ev_e[dom])]
     kern_ms_mean = sum(kern_ms) / len(kern_ms)
 
     bytes_step = sum(a["bytes"] for a in arms)
@@ -209,8 +215,10 @@ def main() -> int:
                    "delta": wl.delta, "decay": "diag" if wl.decay else "scalar",
                    "arms": [{"name": a["arm"].name, "bits": a["cfg"].bits,
                              "group": a["cfg"].group, "policy": a["cfg"].policy,
-                             "rounding": a["cfg"].rounding, "heads": a["cfg"].n,
-                             "bytes_per_step": a["bytes"]} for a in arms],
+                             "rounding": a["cfg"].rounding, "scale_fmt": a["cfg"].scale_fmt,
+                             "lrb_rank": a["cfg"].lrb_rank, "heads": a["cfg"].n,
+                             "bytes_per_step": a["bytes"], "launch_us": a["launch_us"],
+                             "kernel_gbs": a["kernel_gbs"]} for a in arms],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
@@ -422,7 +430,27 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
     b, hs, dt = run(steps)
     heads = sum(o.n for _, o, _, _ in samples)
     log(f"cpu oracle: {heads} sampled heads x {steps} steps in {dt:.1f} s on {threads} threads")
+    # one core, one step of the first arm's sample; and the rounding statistics
+    # of one oracle step on every arm's sample (element-steps changed by
+    # directional rounding, and clamped at qmax)
+    a0, o0, s0, sel0 = samples[0]
+    x0 = {k: a0["inp"][k][:1].index_select(1, sel0).cpu().numpy() for k in a0["inp"]}
+    one_core = None
+    if o0.lrb_rank == 0:
+        t1 = time.perf_counter()
+        oracle.run(o0, s0.copy(), x0["q"], x0["k"], x0["v"], x0["alpha"], x0["beta"], nthreads=1)
+        dt_one = time.perf_counter() - t1
+        one_core = round(runner.algorithmic_bytes(a0["cfg"]) // a0["cfg"].n * o0.n / dt_one / 1e9, 4)
+    rates = []
+    for a, ocfg, st, sel in samples:
+        x = {k: a["inp"][k][0].index_select(0, sel).cpu().numpy() for k in a["inp"]}
+        stats = {}
+        oracle.step(ocfg, st.copy(), x["q"], x["k"], x["v"], x["alpha"], x["beta"], stats=stats)
+        ne = ocfg.n * ocfg.dv * ocfg.dk
+        rates.append({"arm": a["arm"].name, "bdr_fired_rate": round(stats["bdr_fired"] / ne, 5),
+                      "clamp_rate": round(stats["clamped"] / ne, 5)})
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "value_one_core": one_core, "rounding_stats": rates,
             "head_steps_per_s": round(hs / dt, 1),
             "sample": f"{heads} heads (1/32 of every arm, evenly spaced) x {steps} steps of the "
                       f"same workload, from the GPU's state, on the same inputs"}
