@@ -66,6 +66,8 @@ def main() -> int:
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--fp32-steps", type=int, default=8,
                     help="steps of the fp32-state comparison run (0 disables it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also replay K more steps captured in one HIP graph (launch gaps removed)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -101,7 +103,7 @@ def main() -> int:
         if wl.shared_inputs and shared is not None:
             inp = shared
         else:
-            inp = runner.inputs(wl, arm, t_first, W + K, npl, dev)
+            inp = runner.inputs(wl, arm, t_first, W + K + (K if args.graph else 0), npl, dev)
             if wl.shared_inputs:
                 shared = inp
         o = torch.empty((cfg.n, cfg.dv), device=dev)
@@ -113,10 +115,10 @@ def main() -> int:
     log(f"set-up {time.perf_counter() - t_setup:.1f} s")
     dom = max(range(len(arms)), key=lambda i: arms[i]["bytes"])
 
-    def launch(a, t):
+    def launch(a, t, s=stream):
         i = a["inp"]
         lsq.lsq_decode_step(a["st"].handle, i["q"][t], i["k"][t], i["v"][t], i["alpha"][t],
-                            i["beta"][t], a["o"], a["o_ref"], stream)
+                            i["beta"][t], a["o"], a["o_ref"], s)
 
     for t in range(W):
         for a in arms:
@@ -153,6 +155,28 @@ def main() -> int:
     dom_gbs = dom_a["bytes"] / (kern_ms_mean * 1e-3) / 1e9
     log(f"timed {K} steps: {wall * 1e3 / K:.3f} ms/step, {gbs:.1f} GB/s; dominant kernel "
         f"{kern_ms_mean * 1e3:.1f} us, {dom_gbs:.1f} GB/s")
+
+    # ---- optional: the next K steps captured in one HIP graph and replayed once
+    # (every launch records its own inputs, step index and bypass slot at
+    # capture; the state advances on replay)
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for t in range(W + K, W + 2 * K):
+                for a in arms:
+                    launch(a, t, cs)
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - tg0
+        graph = {"steps": K, "ms_per_step": round(gwall * 1e3 / K, 4),
+                 "value": round(sum(a["bytes"] for a in arms) * K / gwall / 1e9, 2)}
+        log(f"graph replay of {K} steps: {gwall * 1e3 / K:.4f} ms/step")
+        del g
 
     traffic = None
     sha = kernel_source_sha()
@@ -228,6 +252,7 @@ def main() -> int:
                      "launch_us_min": round(min(kern_ms) * 1e3, 2),
                      "source_sha": sha},
         "fp32_state": fp32,
+        "graph_replay": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
