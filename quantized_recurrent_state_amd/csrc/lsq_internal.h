@@ -91,6 +91,8 @@ hipError_t launch_step_f32(const StepArgs& a, int dk, int delta, int diag, hipSt
 hipError_t launch_calibrate(const CalibArgs& a, int bits, int dk, hipStream_t s);
 hipError_t launch_lrb_step(const StepArgs& a, int bits, int dk, int policy, int rounding,
                            int delta, int diag, hipStream_t s);
+hipError_t launch_lrb_step_r8(const StepArgs& a, int bits, int dk, int policy, int rounding,
+                              int delta, int diag, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int bits, int dk, int dv, int policy, int diag,
                           hipStream_t s);
 hipError_t launch_bdr_alt(const StepArgs& a, int bits, int dk, int rounding, int delta, int diag,

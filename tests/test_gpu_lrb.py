@@ -21,19 +21,21 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _inputs(recipe, n, dk, dv, steps, seed=4):
+def _inputs(recipe, n, dk, dv, steps, seed=4, edit=None):
     d = gen_steps(recipe, n, dk, dv, [seed], 0, steps, device="cpu")
+    if edit is not None:
+        edit(d)
     return {k: v.to(DEV) for k, v in d.items()}, {k: v.numpy() for k, v in d.items()}
 
 
-def _run(cfg, steps, recipe, t0=0):
+def _run(cfg, steps, recipe, t0=0, edit=None):
     R = cfg.lrb_rank
     st = lsq.LsqState(cfg, device=DEV).zero()
     if cfg.policy == lsq.POLICY_PERSISTENT:
         g = torch.Generator(device=DEV).manual_seed(1)
         st.calibrate(torch.randn(cfg.n, cfg.dv, cfg.dk, device=DEV, generator=g) * 0.3)
     st.step_index = t0
-    dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, steps)
+    dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, steps, edit=edit)
     rep = Report()
     diag = cfg.decay == lsq.DECAY_DIAG
     for t in range(steps):
@@ -87,3 +89,21 @@ def test_bypass_ranks_and_offsets(R):
                         decay=lsq.DECAY_SCALAR, lrb_rank=R)
     rep = _run(cfg, R + 3, "gdn", t0=5 * R + 1)     # start mid-period
     assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("bits,pol,dl,dc", [(b, p, dl, dc) for b in (4, 8)
+                                            for p in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+                                            for dl in (0, 1)
+                                            for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)])
+def test_bypass_merge_without_update_direction(bits, pol, dl, dc):
+    """Merges where the buffer's value U is exactly zero (k columns zero in
+    every step, heads with beta = 0): those elements round to nearest."""
+    from tests.test_gpu_parity import zero_directions
+    R = 3
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=128, dv=44, bits=bits, group=32 if bits == 4 else 64,
+                        policy=pol, rounding=lsq.ROUND_BDR, delta=dl, decay=dc, lrb_rank=R)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run(cfg, 2 * R + 1, recipe, edit=lambda d: zero_directions(d, 128))
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)

@@ -20,16 +20,27 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _inputs(recipe, n, dk, dv, t0, steps, seed=0):
+def _inputs(recipe, n, dk, dv, t0, steps, seed=0, edit=None):
     d = gen_steps(recipe, n, dk, dv, [seed], t0, steps, device="cpu")
+    if edit is not None:
+        edit(d)
     return {k: v.to(DEV) for k, v in d.items()}, {k: v.numpy() for k, v in d.items()}
+
+
+def zero_directions(d, dk):
+    """Inputs with no update direction in places: k columns that are exactly
+    zero in every step and head (including a column inside the last lane's
+    chunk and one on a group edge), and heads whose beta is zero (w = 0)."""
+    for c in (0, 5, dk // 2, dk - 1):
+        d["k"][:, :, c] = 0.0
+    d["beta"][:, 1::3] = 0.0
 
 
 def _np_step(d, t):
     return (d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t])
 
 
-def _run_teacher_forced(cfg, steps, recipe, warmup=4):
+def _run_teacher_forced(cfg, steps, recipe, warmup=4, edit=None):
     """Run the GPU path, comparing each step with the oracle from the GPU's state."""
     ocfg = ocfg_of(cfg)
     st = lsq.LsqState(cfg, device=DEV).zero()
@@ -38,7 +49,7 @@ def _run_teacher_forced(cfg, steps, recipe, warmup=4):
     if cfg.policy == lsq.POLICY_PERSISTENT:
         f = lsq.LsqState(lsq.LsqConfig(cfg.batch, cfg.heads, cfg.dk, cfg.dv, 32, 1,
                                        lsq.POLICY_NONE, 0, cfg.delta, cfg.decay), device=DEV).zero()
-        dg, _ = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, 0, warmup)
+        dg, _ = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, 0, warmup, edit=edit)
         f.run(dg["q"], dg["k"], dg["v"], dg["alpha"], dg["beta"])
         st.calibrate(f.f32)
         # calibration itself: bit-exact against the oracle's quantiser
@@ -47,7 +58,7 @@ def _run_teacher_forced(cfg, steps, recipe, warmup=4):
         assert np.array_equal(got.codes, want.codes)
         assert np.array_equal(got.scales, want.scales)
         t0 = warmup
-    dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, t0, steps)
+    dg, dn = _inputs(recipe, cfg.n, cfg.dk, cfg.dv, t0, steps, edit=edit)
     before = snapshot(st)
     if cfg.rounding == lsq.ROUND_DITHER:
         st.step_index = 1000 + 37 * cfg.dk     # any position: the sequence is stateless
@@ -78,6 +89,29 @@ def test_step_matches_oracle(bits, dk, pol, rnd, dl, dc):
                         policy=pol, rounding=rnd, delta=dl, decay=dc)
     recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
     rep = _run_teacher_forced(cfg, steps=6, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
+ZD = [(bits, dk, pol, dl, dc)
+      for bits in (4, 8)
+      for dk in (128, 64)
+      for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+      for dl in (0, 1)
+      for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,dl,dc", ZD)
+def test_bdr_without_update_direction(bits, dk, pol, dl, dc):
+    """Directional rounding where the update has no sign (k_c = 0, or w = 0
+    for a head with beta = 0): those elements round to nearest."""
+    group = 32 if bits == 4 else 64
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=44, bits=bits, group=min(group, dk),
+                        policy=pol, rounding=lsq.ROUND_BDR, delta=dl, decay=dc)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=5, recipe=recipe,
+                              edit=lambda d: zero_directions(d, dk))
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
     assert rep.excused <= max(2, rep.codes // 20000), str(rep)
