@@ -316,9 +316,11 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
             for (int e8 = 0; e8 < 8; ++e8) {
               const float c1 = t[e8] - F::MQ;                     // exact
               const float d = fmaf(sp[8 * b + e8], inv, -c1);     // sign of y' - c1, exact
-              const bool up = U8[e8] > 0.f && d > 0.f;
-              const bool dn = U8[e8] < 0.f && d < 0.f;
-              const float step = up ? 1.f : (dn ? -1.f : 0.f);    // branch-free
+              // d times the sign of U (a sign-bit flip), and copysign(1, U)
+              const uint32_t su = fbits(U8[e8]) & 0x80000000u;
+              const float ds = __uint_as_float(fbits(d) ^ su);
+              const float sg = __uint_as_float(0x3F800000u | su);
+              const float step = (ds > 0.f && U8[e8] != 0.f) ? sg : 0.f;   // branch-free
               t[e8] = __builtin_amdgcn_fmed3f(t[e8] + step, F::MQ - F::QMAX, F::MQ + F::QMAX);
             }
           }
