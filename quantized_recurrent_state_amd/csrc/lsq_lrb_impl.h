@@ -18,7 +18,8 @@
 // b_j sit in LDS; the slot projections b_j . k, b_j . q and k . q are reduced
 // once per wave and, being the same on every lane, kept in scalar registers.
 // Row data (codes, scale, v and the row's a_j) is addressed from wave-uniform
-// head bases and loaded one row ahead.  On a merge step under a frozen scale
+// head bases; rows go in pairs with two prefetch buffers, so the next row's
+// loads are in flight while a row is computed.  On a merge step under a frozen scale
 // each block of eight elements is merged, rounded and packed before the next
 // is built, so X and U never occupy more than a block's registers.  Buffer
 // memory per head: a [r][Dv]; b [2][r][Dk], the second copy used by diagonal
@@ -159,10 +160,8 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
 #pragma unroll
     for (int j = 0; j < RMAX; ++j) d.aj[j] = (j < nu) ? at_bytes(ah, ((uint32_t)j * dv + i) * 4u) : 0.f;
   };
-  RowData cur, nxt;
-  load_row_data(0, cur);
-  for (int it = 0; it < a.nit; ++it) {
-    if (it + 1 < a.nit) load_row_data(it + 1, nxt);
+  // One row, from dequantisation to the packed store.
+  auto process = [&](const RowData& cur, int it) {
     const uint32_t r = (uint32_t)((slice * a.nit + it) * RPI + lr);
     const bool live = r < dv;
     const uint32_t i = live ? r : dv - 1;
@@ -351,7 +350,17 @@ __global__ __launch_bounds__(256) void lrb_step_kernel(StepArgs a) {
         at_bytes(ah, ((uint32_t)nu * dv + i) * 4u) = w;
       }
     }
-    cur = nxt;
+  };
+
+  // Rows in pairs with two prefetch buffers (no register copies between rows).
+  RowData bufA, bufB;
+  load_row_data(0, bufA);
+  for (int it = 0; it < a.nit; it += 2) {
+    if (it + 1 < a.nit) load_row_data(it + 1, bufB);
+    process(bufA, it);
+    if (it + 1 >= a.nit) break;
+    if (it + 2 < a.nit) load_row_data(it + 2, bufA);
+    process(bufB, it + 1);
   }
 }
 
