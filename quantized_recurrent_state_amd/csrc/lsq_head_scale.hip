@@ -167,6 +167,143 @@ __global__ __launch_bounds__(256) void head_scale_kernel(StepArgs a) {
   }
 }
 
+// The same step for heads of at most 8 x (rows per wave-iteration) rows (128
+// at Dk = 128): one workgroup of eight waves per head, one row-iteration per
+// wave, so every row's S' and S stay in registers across the workgroup
+// barrier and the codes are read once.  k, q and a diagonal decay are staged
+// in LDS.  Pass 1 (update, o, running max) and pass 2 (requantisation) are
+// the two halves of the same per-row computation as above; the values, the
+// rounding and the stored results are the same.
+constexpr int kHeadWaves1 = 8;
+
+template <int BITS, int DK, int ROUND, int DELTA, int DIAG>
+__global__ __launch_bounds__(512) void head_scale1_kernel(StepArgs a) {
+  using F = Fmt<BITS>;
+  constexpr int NW = F::NW, LPR = DK / EPL, RPI = 64 / LPR, ROWB = DK * BITS / 8;
+  constexpr bool BDR = ROUND == RND_BDR;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x;
+  const int lr = lane / LPR, lc = lane % LPR, col0 = lc * EPL;
+  __shared__ float4 vec4[(DIAG ? 3 : 2) * DK / 4];
+  __shared__ float wmax[kHeadWaves1];
+  float* kv = reinterpret_cast<float*>(vec4);
+  float* qv = kv + DK;
+  float* av = kv + 2 * DK;
+
+  // this lane's row: its codes and v are requested before the vectors are staged
+  const int r = wave * RPI + lr;
+  const bool live = r < a.dv;
+  const uint32_t i = (uint32_t)(live ? r : a.dv - 1);
+  uint8_t* const codes_h = a.codes + (size_t)h * a.dv * ROWB;
+  uint32_t xo[NW];
+#pragma unroll
+  for (int c = 0; c < NW / 4; ++c) {
+    const u32x4 w4 = load_codes16(codes_h + (i * ROWB + lc * (EPL * BITS / 8) + 16 * c));
+    xo[4 * c + 0] = w4.x ^ F::OFF;
+    xo[4 * c + 1] = w4.y ^ F::OFF;
+    xo[4 * c + 2] = w4.z ^ F::OFF;
+    xo[4 * c + 3] = w4.w ^ F::OFF;
+  }
+  const float vr = a.v[(size_t)h * a.dv + i];
+  const float s = a.scales[h];
+  const float beta = a.beta[h];
+  const float alpha_s = DIAG ? 1.f : a.alpha[h];
+  if (tid < DK) {
+    kv[tid] = a.k[(size_t)h * DK + tid];
+    qv[tid] = a.q[(size_t)h * DK + tid];
+    if constexpr (DIAG) av[tid] = a.alpha[(size_t)h * DK + tid];
+  }
+  __syncthreads();
+
+  // pass 1: S' = fl(C fl(s alpha)), u, w, S = fma(w, k, S'), o, max |S|
+  float sp[EPL];
+  if constexpr (DIAG) {
+    unpack_offsets<BITS>(xo, sp);
+#pragma unroll
+    for (int b = 0; b < EPL / 8; ++b) {
+      float ab[8];
+      lds_block<DK>(ab, av, col0 + 8 * b);
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) sp[8 * b + e8] = (sp[8 * b + e8] - F::BIAS) * (s * ab[e8]);
+    }
+  } else {
+    const float m[1] = {s * alpha_s}, mb[1] = {-F::BIAS * (s * alpha_s)};
+    dequant_mix<BITS, 1>(xo, m, mb, sp);
+  }
+  float u = 0.f;
+  if constexpr (DELTA) {
+    float pu = 0.f;
+#pragma unroll
+    for (int b = 0; b < EPL / 8; ++b) {
+      float kb[8];
+      lds_block<DK>(kb, kv, col0 + 8 * b);
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) pu = fmaf(sp[8 * b + e8], kb[e8], pu);
+    }
+    u = row_sum<LPR>(pu);
+  }
+  const float w = beta * (vr - u);
+  float st[EPL];
+  float po = 0.f, amax = 0.f;
+#pragma unroll
+  for (int b = 0; b < EPL / 8; ++b) {
+    float kb[8], qb[8];
+    lds_block<DK>(kb, kv, col0 + 8 * b);
+    lds_block<DK>(qb, qv, col0 + 8 * b);
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      st[8 * b + e8] = fmaf(w, kb[e8], sp[8 * b + e8]);
+      po = fmaf(st[8 * b + e8], qb[e8], po);
+      amax = fmaxf(amax, fabsf(st[8 * b + e8]));
+    }
+  }
+  const float o = row_sum<LPR>(po);
+  if (live && lc == 0) a.o[(size_t)h * a.dv + i] = o;
+  if (!live) amax = 0.f;
+  amax = wave_max_all(amax);
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  float mx = wmax[0];
+#pragma unroll
+  for (int j = 1; j < kHeadWaves1; ++j) mx = fmaxf(mx, wmax[j]);
+  const float snew = mx / F::QMAX;
+  const float inv = inv_scale(snew);
+
+  // pass 2: round half to even, or directional rounding (sigma = sign(w) sign(k_c);
+  // a code c1 with (c1 - S' inv) sigma < 0, decided by the sign of one fma,
+  // becomes c1 + sigma, clamped)
+  const int sw = (w > 0.f) - (w < 0.f);
+  float t[EPL];
+#pragma unroll
+  for (int b = 0; b < EPL / 8; ++b) {
+    float kb[8];
+    if constexpr (BDR) lds_block<DK>(kb, kv, col0 + 8 * b);
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const int e = 8 * b + e8;
+      t[e] = __builtin_amdgcn_fmed3f(fmaf(st[e], inv, F::MQ), F::MQ - F::QMAX, F::MQ + F::QMAX);
+      if constexpr (BDR) {
+        const int sigma = sw * ((kb[e8] > 0.f) - (kb[e8] < 0.f));
+        const float d = fmaf(sp[e], inv, F::MQ - t[e]);     // S' inv - c1, one rounding
+        const bool rev = (sigma > 0 && d > 0.f) || (sigma < 0 && d < 0.f);
+        const float step = rev ? (float)sigma : 0.f;
+        t[e] = __builtin_amdgcn_fmed3f(t[e] + step, F::MQ - F::QMAX, F::MQ + F::QMAX);
+      }
+    }
+  }
+  uint32_t X[NW];
+  pack_offsets<BITS>(t, X);
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < NW / 4; ++c)
+      store_codes16(codes_h + (i * ROWB + lc * (EPL * BITS / 8) + 16 * c),
+                    u32x4{X[4 * c] ^ F::OFF, X[4 * c + 1] ^ F::OFF, X[4 * c + 2] ^ F::OFF,
+                          X[4 * c + 3] ^ F::OFF});
+  }
+  if (tid == 0) a.scales[h] = snew;
+}
+
 // Calibration with one scale per head: absmax over the head, then RNE codes.
 template <int BITS, int DK>
 __global__ __launch_bounds__(256) void calibrate_head_kernel(CalibArgs a) {
@@ -219,6 +356,22 @@ __global__ __launch_bounds__(256) void calibrate_head_kernel(CalibArgs a) {
 
 hipError_t launch_head_scale(const StepArgs& a, int bits, int dk, int policy, int rounding,
                              int delta, int diag, hipStream_t s) {
+  // heads of at most eight row-iterations: one per wave, the rows held in registers
+  if (policy == dev::POL_DYNAMIC && a.dv <= dev::kHeadWaves1 * (64 / (dk / dev::EPL))) {
+    const dim3 grid1(a.n_heads), block1(64 * dev::kHeadWaves1);
+#define LSQ_HS1(B, DK, R, D, G)                                                                 \
+    if (bits == B && dk == DK && rounding == R && delta == D && diag == G) {                    \
+      hipLaunchKernelGGL((dev::head_scale1_kernel<B, DK, R, D, G>), grid1, block1, 0, s, a);    \
+      return hipGetLastError();                                                                 \
+    }
+#define LSQ_HS1_R(B, DK, R) LSQ_HS1(B, DK, R, 0, 0) LSQ_HS1(B, DK, R, 0, 1) LSQ_HS1(B, DK, R, 1, 0) LSQ_HS1(B, DK, R, 1, 1)
+#define LSQ_HS1_DK(B, DK) LSQ_HS1_R(B, DK, dev::RND_RNE) LSQ_HS1_R(B, DK, dev::RND_BDR)
+    LSQ_HS1_DK(4, 128) LSQ_HS1_DK(4, 64) LSQ_HS1_DK(8, 128) LSQ_HS1_DK(8, 64)
+#undef LSQ_HS1_DK
+#undef LSQ_HS1_R
+#undef LSQ_HS1
+    return hipErrorInvalidValue;
+  }
   const dim3 grid(a.n_heads), block(64 * dev::kHeadWaves);
 #define LSQ_HS(B, DK, P, R, D, G)                                                               \
   if (bits == B && dk == DK && policy == P && rounding == R && delta == D && diag == G) {      \
