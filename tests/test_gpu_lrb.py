@@ -107,3 +107,19 @@ def test_bypass_merge_without_update_direction(bits, pol, dl, dc):
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
     assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
+@pytest.mark.parametrize("R,bits,pol,rnd,dc", [
+    (5, 4, lsq.POLICY_DYNAMIC, lsq.ROUND_BDR, lsq.DECAY_DIAG),
+    (6, 8, lsq.POLICY_DYNAMIC, lsq.ROUND_RNE, lsq.DECAY_SCALAR),
+    (7, 8, lsq.POLICY_PERSISTENT, lsq.ROUND_BDR, lsq.DECAY_SCALAR),
+    (5, 4, lsq.POLICY_PERSISTENT, lsq.ROUND_DITHER, lsq.DECAY_DIAG),
+])
+def test_bypass_large_ranks(R, bits, pol, rnd, dc):
+    """Ranks 5 to 8 take their own kernel instances: other flags than the rank-8 case above."""
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=128, dv=44, bits=bits, group=32 if bits == 4 else 64,
+                        policy=pol, rounding=rnd, delta=1, decay=dc, lrb_rank=R)
+    rep = _run(cfg, R + 2, "gla" if dc == lsq.DECAY_DIAG else "gdn", t0=2 * R - 1)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
