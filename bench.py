@@ -74,7 +74,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures the decode step on one GPU only; the step needs "
+        print("bench.py: this benchmark measures the decode step on one GPU only; the step needs "
               "no exchange between GPUs, and runs with --gpus above 1 are not part of it",
               file=sys.stderr)
         return 2

@@ -111,7 +111,7 @@ extern "C" {
 typedef enum {
   LSQ_OK = 0,
   LSQ_ERR_INVALID_ARG = 1,     /* null pointer, bad value, misaligned buffer */
-  LSQ_ERR_UNSUPPORTED = 2,     /* a valid configuration this build has no kernel for */
+  LSQ_ERR_UNSUPPORTED = 2,     /* a valid configuration this library has no kernel for */
   LSQ_ERR_BUFFER_TOO_SMALL = 3,
   LSQ_ERR_NOT_CALIBRATED = 4,  /* persistent policy stepped before its scales were frozen */
   LSQ_ERR_HIP = 5              /* a HIP runtime call or kernel launch failed */
@@ -139,7 +139,7 @@ typedef enum { LSQ_SCALE_F32 = 0, LSQ_SCALE_F16 = 1, LSQ_SCALE_BF16 = 2 } lsq_sc
 
 /* Shape, format and method flags of one handle.
  *   bits   4, 8 (quantised) or 32 (fp32 state, policy NONE)
- *   group  group size along Dk; must divide dk.  This build supports
+ *   group  group size along Dk; must divide dk.  This library supports
  *          power-of-two groups of 16 to Dk elements (one lane owns 32
  *          consecutive elements of a row: one group, part of one, or two
  *          16-element groups) and Dk in {64, 128}.  group = Dk is one scale

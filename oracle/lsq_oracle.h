@@ -130,7 +130,7 @@ int lsqo_step(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref, 
 
 /* lsqo_step that also records, for every quantised element, the exact
  * pre-rounding values in code units: y = S_t * inv and y' = S' * inv (both
- * nullable together).  Used to judge whether a differing code lies at a
+ * nullable together).  Used to decide whether a differing code lies at a
  * rounding boundary. */
 int lsqo_step_trace(const lsqo_config* cfg, int8_t* codes, float* scales, float* ref,
                     float* f32, const float* q, const float* k, const float* v,

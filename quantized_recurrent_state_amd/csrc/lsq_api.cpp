@@ -79,7 +79,7 @@ lsq_status check_config(const lsq_config* c) {
   } else {
     return fail(LSQ_ERR_INVALID_ARG, "bits must be 4, 8 or 32");
   }
-  if (c->dk != 64 && c->dk != 128) return fail(LSQ_ERR_UNSUPPORTED, "dk %d: this build has dk 64 and 128", c->dk);
+  if (c->dk != 64 && c->dk != 128) return fail(LSQ_ERR_UNSUPPORTED, "dk %d: this library has dk 64 and 128", c->dk);
   if (c->bits != 32 && c->group == 0) {
     if (c->scale_fmt != LSQ_SCALE_F32 || c->lrb_rank != 0)
       return fail(LSQ_ERR_UNSUPPORTED, "one scale per head runs with an fp32 scale and no bypass");
@@ -88,7 +88,7 @@ lsq_status check_config(const lsq_config* c) {
     constexpr int min_group = 16;   // a lane owns 32 elements: one group, or two of 16
     if (c->group < min_group || (c->group & (c->group - 1)) != 0)
       return fail(LSQ_ERR_UNSUPPORTED,
-                  "group %d: this build needs a power-of-two group of at least %d elements",
+                  "group %d: this library needs a power-of-two group of at least %d elements",
                   c->group, min_group);
   }
   if (c->scale_fmt != LSQ_SCALE_F32 && c->scale_fmt != LSQ_SCALE_F16 &&
@@ -442,7 +442,7 @@ const char* lsq_status_string(lsq_status s) {
   switch (s) {
     case LSQ_OK: return "LSQ_OK";
     case LSQ_ERR_INVALID_ARG: return "LSQ_ERR_INVALID_ARG: invalid argument";
-    case LSQ_ERR_UNSUPPORTED: return "LSQ_ERR_UNSUPPORTED: configuration not supported by this build";
+    case LSQ_ERR_UNSUPPORTED: return "LSQ_ERR_UNSUPPORTED: configuration not supported by this library";
     case LSQ_ERR_BUFFER_TOO_SMALL: return "LSQ_ERR_BUFFER_TOO_SMALL: a state buffer is too small";
     case LSQ_ERR_NOT_CALIBRATED: return "LSQ_ERR_NOT_CALIBRATED: persistent scales not calibrated";
     case LSQ_ERR_HIP: return "LSQ_ERR_HIP: HIP runtime error";
