@@ -223,6 +223,22 @@ def main() -> int:
         del fl
         log(f"fp32-state step {fms:.3f} ms")
 
+    # ---- arms on shared inputs beside a yoked arm: the stored state's Frobenius
+    # norm (lsq_state_dequantize, fl(C s)) against the fp32 reference R the yoked
+    # arm advances on the same inputs, after the same steps; reported, not a bound
+    state_norms = None
+    yoked = [a for a in arms if a["cfg"].policy == lsq.POLICY_YOKED]
+    if wl.shared_inputs and yoked:
+        r_norm = float(torch.linalg.vector_norm(yoked[0]["st"].ref, dtype=torch.float64))
+        state_norms = {"reference": "fp32 R of the yoked arm",
+                       "steps": int(yoked[0]["st"].step_index), "ratio_to_reference": {}}
+        for a in arms:
+            S = a["st"].dequantize()
+            state_norms["ratio_to_reference"][a["arm"].name] = round(
+                float(torch.linalg.vector_norm(S, dtype=torch.float64)) / r_norm, 5)
+            del S
+        log(f"state norm / reference norm: {state_norms['ratio_to_reference']}")
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     if args.cpu_seconds > 0:
@@ -253,6 +269,7 @@ def main() -> int:
                      "source_sha": sha},
         "fp32_state": fp32,
         "graph_replay": graph,
+        "state_norms": state_norms,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -211,6 +211,17 @@ lsq_status lsq_state_zero(lsq_state* st, void* stream);
  * "plain persistent scaling" ("When Dynamic Scaling Fails", abstract). */
 lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream);
 
+/* The dequantised state: S [heads][Dv][Dk] fp32 (device, caller-owned, 16-byte
+ * aligned) receives fl(C s) for every element, C the stored code and s its
+ * group's scale in the stored format (or the head's scale for group 0), the
+ * value a step starts from before its decay ("Preserving Updates in Low-Bit
+ * Recurrent State Quantization", abstract: the low-bit state stands for the
+ * full-precision one; its norm against an fp32 reference is the quantity of
+ * "When Dynamic Scaling Fails", norm-inflation figure).  bits 32 copies the
+ * fp32 state.  Asynchronous on stream; the handle is not changed.
+ * INVALID_ARG for a null or misaligned S. */
+lsq_status lsq_state_dequantize(const lsq_state* st, float* S, void* stream);
+
 /* Declare that the bound scale buffer already holds frozen scales (resuming a
  * persistent-policy state from a copy of its buffers). */
 lsq_status lsq_state_set_calibrated(lsq_state* st, int32_t calibrated);

@@ -21,7 +21,7 @@ DECAY_SCALAR, DECAY_DIAG = 0, 1
 SCALE_F32, SCALE_F16, SCALE_BF16 = 0, 1, 2
 
 __all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_alloc",
-           "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_set_calibrated",
+           "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_dequantize", "lsq_state_set_calibrated",
            "lsq_state_step_index", "lsq_state_set_step_index",
            "lsq_decode_step", "lsq_decode_run", "lsq_prefill", "lsq_status_string", "lsq_version"]
 
@@ -94,6 +94,11 @@ def lsq_state_zero(handle: int, stream=None) -> None:
 def lsq_state_calibrate(handle: int, S, stream=None) -> None:
     _lib.check(_lib.load().lsq_state_calibrate(handle, _ptr(S), _stream_ptr(stream)),
                "lsq_state_calibrate")
+
+
+def lsq_state_dequantize(handle: int, S, stream=None) -> None:
+    _lib.check(_lib.load().lsq_state_dequantize(handle, _ptr(S), _stream_ptr(stream)),
+               "lsq_state_dequantize")
 
 
 def lsq_state_set_calibrated(handle: int, calibrated: bool = True) -> None:
@@ -195,6 +200,16 @@ class LsqState:
         _check_tensor("S", S, (self.cfg.n, self.cfg.dv, self.cfg.dk))
         lsq_state_calibrate(self.handle, S, stream)
         return self
+
+    def dequantize(self, out=None, stream=None):
+        """fl(C s) of every element as an fp32 tensor [n, dv, dk] (the stored state)."""
+        import torch
+        if out is None:
+            out = torch.empty((self.cfg.n, self.cfg.dv, self.cfg.dk), device=self.device,
+                              dtype=torch.float32)
+        _check_tensor("out", out, (self.cfg.n, self.cfg.dv, self.cfg.dk))
+        lsq_state_dequantize(self.handle, out, stream)
+        return out
 
     def set_calibrated(self, calibrated=True):
         lsq_state_set_calibrated(self.handle, calibrated)

@@ -60,6 +60,7 @@ def load() -> ctypes.CDLL:
         "lsq_state_config": [P, cfgp],
         "lsq_state_zero": [P, P],
         "lsq_state_calibrate": [P, P, P],
+        "lsq_state_dequantize": [P, P, P],
         "lsq_state_set_calibrated": [P, ctypes.c_int32],
         "lsq_state_step_index": [P, ctypes.POINTER(ctypes.c_int64)],
         "lsq_state_set_step_index": [P, ctypes.c_int64],

@@ -296,6 +296,29 @@ lsq_status lsq_state_zero(lsq_state* st, void* stream) {
   return ok();
 }
 
+lsq_status lsq_state_dequantize(const lsq_state* st, float* S, void* stream) {
+  if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
+  const lsq_config& c = st->cfg;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t elems = (size_t)n_heads(c) * c.dv * c.dk;
+  if (elems == 0) return ok();
+  if (!S) return fail(LSQ_ERR_INVALID_ARG, "S is null");
+  if (!aligned16(S)) return fail(LSQ_ERR_INVALID_ARG, "S must be 16-byte aligned");
+  if (c.bits == 32)                    // the state is already fp32
+    return hip_status(hipMemcpyAsync(S, st->f32, elems * 4, hipMemcpyDeviceToDevice, hs),
+                      "dequantize copy");
+  lsq::DequantArgs a{};
+  a.codes = static_cast<const uint8_t*>(st->codes);
+  a.scales = st->scales;
+  a.S = S;
+  a.rows = (int64_t)n_heads(c) * c.dv;
+  a.dv = c.dv;
+  a.group = c.group;
+  a.ng = c.group ? c.dk / c.group : 0;
+  a.sfmt = c.scale_fmt;
+  return hip_status(lsq::launch_dequantize(a, c.bits, c.dk, hs), "dequantize launch");
+}
+
 lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream) {
   if (!st) return fail(LSQ_ERR_INVALID_ARG, "state is null");
   const lsq_config& c = st->cfg;
@@ -452,6 +475,6 @@ const char* lsq_status_string(lsq_status s) {
 
 const char* lsq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t lsq_version(void) { return 102; }
+int32_t lsq_version(void) { return 103; }
 
 }  // extern "C"

@@ -53,6 +53,16 @@ struct CalibArgs {
   int32_t sfmt;          // stored scale format (as StepArgs)
 };
 
+// Arguments of a dequantisation launch: S = fl(C s) of every element.
+struct DequantArgs {
+  const uint8_t* codes;  // [n][dv][dk*bits/8]
+  const void* scales;    // [n][dv][ng] in the stored format, or [n] (one per head)
+  float* S;              // [n][dv][dk]
+  int64_t rows;          // n * dv
+  int32_t dv, group, ng;
+  int32_t sfmt;          // stored scale format (as StepArgs)
+};
+
 // Arguments of a chunkwise prefill launch (linear write): the handle's packed
 // state is advanced over T tokens, one workgroup per head.
 struct PrefillArgs {
@@ -101,5 +111,6 @@ hipError_t launch_head_scale(const StepArgs& a, int bits, int dk, int policy, in
                              int delta, int diag, hipStream_t s);
 hipError_t launch_calibrate_head(const CalibArgs& a, int bits, int dk, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs& a, int bits, int dk, hipStream_t s);
 
 }  // namespace lsq

@@ -201,4 +201,50 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+namespace dev {
+
+// S = fl(C s) for every element: one thread per 16 bytes of codes (32 INT4
+// or 16 INT8 elements of one row), 16-byte loads and stores.
+template <int BITS, int DK>
+__global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
+  constexpr int ROWB = DK * BITS / 8, TPR = ROWB / 16, EPT = 16 * 8 / BITS;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.rows * TPR) return;
+  const int64_t row = t / TPR;
+  const int c0 = (int)(t - row * TPR) * EPT;
+  const uint4 w4 = *reinterpret_cast<const uint4*>(a.codes + row * ROWB + (c0 * BITS) / 8);
+  const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+  float out[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t word = w[(e * BITS) / 32], sh = (e * BITS) % 32;
+    const int code = BITS == 4 ? ((int)(word << (28 - sh)) >> 28) : ((int)(word << (24 - sh)) >> 24);
+    const int64_t si = a.group == 0 ? row / a.dv : row * a.ng + (c0 + e) / a.group;
+    float s;
+    if (a.sfmt == SFMT_F32)
+      s = reinterpret_cast<const float*>(a.scales)[si];
+    else
+      s = scale_from16(reinterpret_cast<const uint16_t*>(a.scales)[si], a.sfmt);
+    out[e] = (float)code * s;
+  }
+  float4* dst = reinterpret_cast<float4*>(a.S + row * DK + c0);
+#pragma unroll
+  for (int e = 0; e < EPT / 4; ++e)
+    dst[e] = make_float4(out[4 * e], out[4 * e + 1], out[4 * e + 2], out[4 * e + 3]);
+}
+
+}  // namespace dev
+
+hipError_t launch_dequantize(const DequantArgs& a, int bits, int dk, hipStream_t s) {
+  const int64_t threads = a.rows * (dk * bits / 8 / 16);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (bits == 4 && dk == 128) hipLaunchKernelGGL((dev::dequantize_kernel<4, 128>), grid, block, 0, s, a);
+  else if (bits == 4 && dk == 64) hipLaunchKernelGGL((dev::dequantize_kernel<4, 64>), grid, block, 0, s, a);
+  else if (bits == 8 && dk == 128) hipLaunchKernelGGL((dev::dequantize_kernel<8, 128>), grid, block, 0, s, a);
+  else if (bits == 8 && dk == 64) hipLaunchKernelGGL((dev::dequantize_kernel<8, 64>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace lsq

@@ -131,6 +131,18 @@ def test_empty_batch_calls_are_noops():
     assert st == 0
     assert L.lsq_decode_step(h, None, None, None, None, None, None, None, None) == 0
     assert L.lsq_state_calibrate(h, None, None) == 0
+    assert L.lsq_state_dequantize(h, None, None) == 0
+    lsq.lsq_state_free(h)
+
+
+def test_dequantize_argument_checks_before_launch():
+    L = _lib.load()
+    cfg = lsq.LsqConfig(1, 2, 128, 16, 4, 32, lsq.POLICY_DYNAMIC)
+    st, h = _alloc(cfg)
+    assert st == 0
+    assert L.lsq_state_dequantize(h, None, None) == 1           # null S
+    assert L.lsq_state_dequantize(h, FAKE + 4, None) == 1       # misaligned S
+    assert L.lsq_state_dequantize(None, FAKE, None) == 1        # null handle
     lsq.lsq_state_free(h)
 
 

@@ -341,3 +341,43 @@ def test_edge_cases():
             torch.ones(2, device=DEV))
     codes = oracle.unpack(st.codes.cpu().numpy(), 4, 128)
     assert np.all(codes == 7)
+
+
+DQ = [(bits, dk, group, fmt)
+      for bits in (4, 8)
+      for dk in (128, 64)
+      for group in (0, 16, 32, 64)
+      for fmt in (0, 1, 2)
+      if not (group == 0 and fmt)]
+
+
+@pytest.mark.parametrize("bits,dk,group,fmt", DQ)
+def test_dequantize_matches_oracle(bits, dk, group, fmt):
+    """lsq_state_dequantize: fl(C s) bit for bit against the oracle's, after a few
+    dynamic steps (per-head scales: persistent, calibrated), ragged Dv."""
+    pol = lsq.POLICY_PERSISTENT if group == 0 else lsq.POLICY_DYNAMIC
+    cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=37, bits=bits, group=group,
+                        policy=pol, rounding=lsq.ROUND_BDR, delta=1, scale_fmt=fmt)
+    try:
+        lsq.lsq_state_sizes(cfg)
+    except lsq.LsqError:
+        pytest.skip(f"not supported: {cfg}")
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    if pol == lsq.POLICY_PERSISTENT:
+        g = torch.Generator(device=DEV).manual_seed(3)
+        st.calibrate(torch.randn(cfg.n, cfg.dv, cfg.dk, device=DEV, generator=g) * 0.2)
+    dg, _ = _inputs("gdn", cfg.n, cfg.dk, cfg.dv, 0, 3)
+    for t in range(3):
+        st.step(dg["q"][t], dg["k"][t], dg["v"][t], dg["alpha"][t], dg["beta"][t])
+    got = st.dequantize().cpu().numpy()
+    want = oracle.dequantize(ocfg_of(cfg), snapshot(st))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.count_nonzero(got) > 0
+
+
+def test_dequantize_fp32_state_is_a_copy():
+    cfg = lsq.LsqConfig(batch=1, heads=2, dk=64, dv=9, bits=32, group=32, policy=lsq.POLICY_NONE)
+    st = lsq.LsqState(cfg, device=DEV).zero()
+    S = torch.randn(cfg.n, cfg.dv, cfg.dk, device=DEV)
+    st.calibrate(S)
+    assert torch.equal(st.dequantize(), S)
