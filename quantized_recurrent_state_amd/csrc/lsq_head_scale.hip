@@ -5,7 +5,10 @@
 // Quantization" (its memory figure leaves the format open) and the per-token
 // dynamic scale of "When Dynamic Scaling Fails" (project page, mechanism
 // paragraph) at head granularity.  A dynamic per-head scale depends on every
-// row's update, so no row can be requantised before all rows are updated: one
+// row's update, so no row can be requantised before all rows are updated.
+// Heads of at most eight row-iterations take head_scale1_kernel (below): one
+// row-iteration per wave of an eight-wave workgroup, every row held in
+// registers across the barrier.  Taller heads take this kernel: one
 // workgroup (four waves) per head makes two passes over the head's rows.
 //   pass 1  per row: codes -> S' = fl(C fl(s alpha)), u = S'.k, w = beta (v -
 //           delta u), S = fma(w, k, S'), o = S.q (written); the row's w kept
