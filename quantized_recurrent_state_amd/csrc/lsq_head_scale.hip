@@ -6,9 +6,9 @@
 // dynamic scale of "When Dynamic Scaling Fails" (project page, mechanism
 // paragraph) at head granularity.  A dynamic per-head scale depends on every
 // row's update, so no row can be requantised before all rows are updated.
-// Heads of at most eight row-iterations take head_scale1_kernel (below): one
-// row-iteration per wave of an eight-wave workgroup, every row held in
-// registers across the barrier.  Taller heads take this kernel: one
+// Heads of at most sixteen row-iterations take head_scale1_kernel (below):
+// one row-iteration per wave of an eight- or sixteen-wave workgroup, every
+// row held in registers across the barrier.  Taller heads take this kernel: one
 // workgroup (four waves) per head makes two passes over the head's rows.
 //   pass 1  per row: codes -> S' = fl(C fl(s alpha)), u = S'.k, w = beta (v -
 //           delta u), S = fma(w, k, S'), o = S.q (written); the row's w kept
@@ -170,17 +170,15 @@ __global__ __launch_bounds__(256) void head_scale_kernel(StepArgs a) {
   }
 }
 
-// The same step for heads of at most 8 x (rows per wave-iteration) rows (128
-// at Dk = 128): one workgroup of eight waves per head, one row-iteration per
-// wave, so every row's S' and S stay in registers across the workgroup
-// barrier and the codes are read once.  k, q and a diagonal decay are staged
+// The same step for heads of at most NWV x (rows per wave-iteration) rows
+// (NWV = 8: 128 rows at Dk = 128; NWV = 16: 256): one workgroup of NWV waves
+// per head, one row-iteration per wave, so every row's S' and S stay in
+// registers across the workgroup barrier and the codes are read once.  k, q and a diagonal decay are staged
 // in LDS.  Pass 1 (update, o, running max) and pass 2 (requantisation) are
 // the two halves of the same per-row computation as above; the values, the
 // rounding and the stored results are the same.
-constexpr int kHeadWaves1 = 8;
-
-template <int BITS, int DK, int ROUND, int DELTA, int DIAG>
-__global__ __launch_bounds__(512) void head_scale1_kernel(StepArgs a) {
+template <int BITS, int DK, int ROUND, int DELTA, int DIAG, int NWV>
+__global__ __launch_bounds__(64 * NWV) void head_scale1_kernel(StepArgs a) {
   using F = Fmt<BITS>;
   constexpr int NW = F::NW, LPR = DK / EPL, RPI = 64 / LPR, ROWB = DK * BITS / 8;
   constexpr bool BDR = ROUND == RND_BDR;
@@ -189,7 +187,7 @@ __global__ __launch_bounds__(512) void head_scale1_kernel(StepArgs a) {
   const int h = blockIdx.x;
   const int lr = lane / LPR, lc = lane % LPR, col0 = lc * EPL;
   __shared__ float4 vec4[(DIAG ? 3 : 2) * DK / 4];
-  __shared__ float wmax[kHeadWaves1];
+  __shared__ float wmax[NWV];
   float* kv = reinterpret_cast<float*>(vec4);
   float* qv = kv + DK;
   float* av = kv + 2 * DK;
@@ -269,7 +267,7 @@ __global__ __launch_bounds__(512) void head_scale1_kernel(StepArgs a) {
   __syncthreads();
   float mx = wmax[0];
 #pragma unroll
-  for (int j = 1; j < kHeadWaves1; ++j) mx = fmaxf(mx, wmax[j]);
+  for (int j = 1; j < NWV; ++j) mx = fmaxf(mx, wmax[j]);
   const float snew = mx / F::QMAX;
   const float inv = inv_scale(snew);
 
@@ -359,12 +357,18 @@ __global__ __launch_bounds__(256) void calibrate_head_kernel(CalibArgs a) {
 
 hipError_t launch_head_scale(const StepArgs& a, int bits, int dk, int policy, int rounding,
                              int delta, int diag, hipStream_t s) {
-  // heads of at most eight row-iterations: one per wave, the rows held in registers
-  if (policy == dev::POL_DYNAMIC && a.dv <= dev::kHeadWaves1 * (64 / (dk / dev::EPL))) {
-    const dim3 grid1(a.n_heads), block1(64 * dev::kHeadWaves1);
+  // heads of at most sixteen row-iterations: one per wave (eight or sixteen
+  // waves), the rows held in registers
+  const int rpi = 64 / (dk / dev::EPL);
+  if (policy == dev::POL_DYNAMIC && a.dv <= 16 * rpi) {
+    const bool w8 = a.dv <= 8 * rpi;
+    const dim3 grid1(a.n_heads), block1(w8 ? 512 : 1024);
 #define LSQ_HS1(B, DK, R, D, G)                                                                 \
     if (bits == B && dk == DK && rounding == R && delta == D && diag == G) {                    \
-      hipLaunchKernelGGL((dev::head_scale1_kernel<B, DK, R, D, G>), grid1, block1, 0, s, a);    \
+      if (w8)                                                                                   \
+        hipLaunchKernelGGL((dev::head_scale1_kernel<B, DK, R, D, G, 8>), grid1, block1, 0, s, a); \
+      else                                                                                      \
+        hipLaunchKernelGGL((dev::head_scale1_kernel<B, DK, R, D, G, 16>), grid1, block1, 0, s, a); \
       return hipGetLastError();                                                                 \
     }
 #define LSQ_HS1_R(B, DK, R) LSQ_HS1(B, DK, R, 0, 0) LSQ_HS1(B, DK, R, 0, 1) LSQ_HS1(B, DK, R, 1, 0) LSQ_HS1(B, DK, R, 1, 1)

@@ -210,11 +210,30 @@ HEAD = [(bits, dk, pol, rnd, dl, dc)
 
 @pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc", HEAD)
 def test_head_scale_matches_oracle(bits, dk, pol, rnd, dl, dc):
-    """One scale per head (group 0): two passes over the head's rows."""
+    """One scale per head (group 0), Dv = 100."""
     cfg = lsq.LsqConfig(batch=2, heads=3, dk=dk, dv=100, bits=bits, group=0, policy=pol,
                         rounding=rnd, delta=dl, decay=dc)
     recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
     rep = _run_teacher_forced(cfg, steps=6, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+
+
+HEAD_DV = [(bits, dk, dv, rnd, dc)
+           for bits, rnd, dc in ((4, lsq.ROUND_BDR, lsq.DECAY_SCALAR), (8, lsq.ROUND_RNE, lsq.DECAY_DIAG))
+           for dk, dvs in ((128, (16, 128, 129, 200, 256, 257, 700)), (64, (256, 300, 512, 513)))
+           for dv in dvs]
+
+
+@pytest.mark.parametrize("bits,dk,dv,rnd,dc", HEAD_DV)
+def test_dynamic_head_scale_heights(bits, dk, dv, rnd, dc):
+    """Dynamic per-head scales over head heights on both sides of the kernel
+    choice: rows held in registers by eight waves (up to 8 row-iterations) or
+    sixteen (up to 16), else two passes."""
+    cfg = lsq.LsqConfig(batch=1, heads=3, dk=dk, dv=dv, bits=bits, group=0,
+                        policy=lsq.POLICY_DYNAMIC, rounding=rnd, delta=1, decay=dc)
+    rep = _run_teacher_forced(cfg, steps=4, recipe="gla" if dc == lsq.DECAY_DIAG else "gdn")
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
     assert rep.excused <= max(2, rep.codes // 20000), str(rep)
