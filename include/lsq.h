@@ -94,8 +94,9 @@
  * happen on the host before any launch and return a status without touching
  * the device.  Launch failures return LSQ_ERR_HIP.  No C++ exception crosses
  * the ABI.  A handle must not be used on two streams at once.  Inputs must be
- * finite and the state far from overflow (scales and |S| below 2^100); the
- * data is not scanned.  With batch*heads == 0 every call is a no-op and its
+ * finite and the state far from overflow (scales and |S| below 2^100); a
+ * nonzero scale must be a normal float (>= 2^-126), since fl(1/s) overflows
+ * below 2^-128 and 0 * inf has no code; the data is not scanned.  With batch*heads == 0 every call is a no-op and its
  * data pointers may be NULL.
  */
 #ifndef LSQ_H
