@@ -430,8 +430,6 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
     from tests.parity import ocfg_of, snapshot
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    if any(a["cfg"].lrb_rank > 0 for a in arms):
-        threads = 1                               # the bypass oracle steps one call at a time
     frac = 1.0 / 32                               # sampled share of every arm's heads
     samples = []
     for a in arms:
@@ -456,9 +454,22 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
             s2 = st.copy()
             t0 = time.perf_counter()
             if ocfg.lrb_rank > 0:
-                for t in range(steps):
-                    oracle.step(ocfg.replace(step=ocfg.step + t), s2, x["q"][t], x["k"][t],
-                                x["v"][t], x["alpha"][t], x["beta"][t])
+                # the bypass oracle steps one call at a time: split the sampled heads
+                # over threads (the oracle releases the interpreter while it runs)
+                import concurrent.futures as cf
+                bounds = np.linspace(0, ocfg.n, threads + 1).astype(np.int64)
+
+                def part(lo, hi):
+                    sub = oracle.OracleState(codes=s2.codes[lo:hi], scales=s2.scales[lo:hi],
+                                             lrb_a=s2.lrb_a[lo:hi], lrb_b=s2.lrb_b[lo:hi])
+                    c = ocfg.replace(batch=int(hi - lo))
+                    for t in range(steps):
+                        oracle.step(c.replace(step=ocfg.step + t), sub, x["q"][t][lo:hi],
+                                    x["k"][t][lo:hi], x["v"][t][lo:hi], x["alpha"][t][lo:hi],
+                                    x["beta"][t][lo:hi])
+
+                with cf.ThreadPoolExecutor(threads) as ex:
+                    list(ex.map(lambda i: part(bounds[i], bounds[i + 1]), range(threads)))
             else:
                 oracle.run(ocfg, s2, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
                            nthreads=threads)
