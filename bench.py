@@ -496,12 +496,19 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
         one_core = round(runner.algorithmic_bytes(a0["cfg"]) // a0["cfg"].n * o0.n / dt_one / 1e9, 4)
     rates = []
     for a, ocfg, st, sel in samples:
-        x = {k: a["inp"][k][0].index_select(0, sel).cpu().numpy() for k in a["inp"]}
-        stats = {}
-        oracle.step(ocfg, st.copy(), x["q"], x["k"], x["v"], x["alpha"], x["beta"], stats=stats)
-        ne = ocfg.n * ocfg.dv * ocfg.dk
-        rates.append({"arm": a["arm"].name, "bdr_fired_rate": round(stats["bdr_fired"] / ne, 5),
-                      "clamp_rate": round(stats["clamped"] / ne, 5)})
+        # one step, or a whole merge period of the bypass (its rounding acts at the merge)
+        nst = max(1, ocfg.lrb_rank)
+        s2, fired, clamped = st.copy(), 0, 0
+        for t in range(nst):
+            x = {k: a["inp"][k][t].index_select(0, sel).cpu().numpy() for k in a["inp"]}
+            stats = {}
+            oracle.step(ocfg.replace(step=ocfg.step + t), s2, x["q"], x["k"], x["v"], x["alpha"],
+                        x["beta"], stats=stats)
+            fired += stats["bdr_fired"]
+            clamped += stats["clamped"]
+        ne = ocfg.n * ocfg.dv * ocfg.dk * nst
+        rates.append({"arm": a["arm"].name, "steps": nst, "bdr_fired_rate": round(fired / ne, 5),
+                      "clamp_rate": round(clamped / ne, 5)})
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "value_one_core": one_core, "rounding_stats": rates,
             "head_steps_per_s": round(hs / dt, 1),
