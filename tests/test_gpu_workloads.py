@@ -67,7 +67,11 @@ def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64):
                 chk = t in check_steps
                 if chk:
                     before = snapshot(st, heads=sels[ai])
-                    step_index = st.step_index          # the dither's sequence position
+                    step_index = st.step_index          # the dither's (and the bypass's) position
+                    if st.cfg.lrb_rank > 0:             # the bypass slots this step reads
+                        cin = (step_index & 1) if st.cfg.decay == lsq.DECAY_DIAG else 0
+                        before.lrb_a = st.lrb_a.index_select(0, sels[ai]).cpu().numpy().copy()
+                        before.lrb_b = st.lrb_b[:, cin].index_select(0, sels[ai]).cpu().numpy().copy()
                 out = st.step(d["q"][j], d["k"][j], d["v"][j], d["alpha"][j], d["beta"][j])
                 if chk:
                     o, o_ref = out if st.cfg.policy == lsq.POLICY_YOKED else (out, None)
@@ -75,7 +79,8 @@ def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64):
                     after = snapshot(st, heads=sel)
                     inp = tuple(d[x][j].index_select(0, sel).cpu().numpy()
                                 for x in ("q", "k", "v", "alpha", "beta"))
-                    ocfg = ocfg_of(st.cfg, step=step_index).replace(batch=len(sel), heads=1)
+                    ocfg = ocfg_of(st.cfg, step=step_index).replace(batch=len(sel), heads=1,
+                                                                    lrb_rank=st.cfg.lrb_rank)
                     reps[ai].add(compare_step(
                         ocfg, before, inp, after, o.index_select(0, sel).cpu().numpy(),
                         None if o_ref is None else o_ref.index_select(0, sel).cpu().numpy()))
@@ -137,7 +142,7 @@ def test_mamba2_bdr_vs_rne():
 
 @pytest.mark.parametrize("key", ["stack24", "stack24-rne", "stack24-dither", "stack24-g16",
                                  "stack24-bf16", "stack24-g16-bf16", "stack24-head", "stack24-bdrb",
-                                 "gdn-head"])
+                                 "stack24-lrb4", "gdn-head"])
 def test_full_size_first_steps(key):
     wl = WORKLOADS[key]
     states, t0 = _prepare(wl, sel_n=48)
