@@ -70,6 +70,8 @@ def main() -> int:
                     help="also replay K more steps captured in one HIP graph (launch gaps removed)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--ceiling-gib", type=float, default=4.0,
+                    help="buffer size of the streaming-ceiling probes (0 disables them)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -178,6 +180,11 @@ def main() -> int:
         log(f"graph replay of {K} steps: {gwall * 1e3 / K:.4f} ms/step")
         del g
 
+    ceiling = None
+    if args.ceiling_gib > 0:
+        span_kib = runner.state_kib_per_head(dom_a["cfg"])
+        ceiling = measure_ceiling(dev, stream, args.ceiling_gib, span_kib)
+
     traffic = None
     sha = kernel_source_sha()
     if os.path.exists(TRAFFIC_FILE):
@@ -266,7 +273,13 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": dom_a["bytes"],
                      "launch_us_mean": round(kern_ms_mean * 1e3, 2),
                      "launch_us_min": round(min(kern_ms) * 1e3, 2),
-                     "source_sha": sha},
+                     "source_sha": sha,
+                     "ceiling_gbs": ceiling and ceiling["copy"]["gbs"],
+                     "frac_of_ceiling": ceiling and round(dom_gbs / ceiling["copy"]["gbs"], 4),
+                     "pattern_ceiling_gbs": ceiling and ceiling["span_in_place"]["gbs"],
+                     "frac_of_pattern_ceiling": ceiling and round(
+                         dom_gbs / ceiling["span_in_place"]["gbs"], 4)},
+        "ceiling": ceiling,
         "fp32_state": fp32,
         "graph_replay": graph,
         "state_norms": state_norms,
@@ -274,6 +287,56 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def measure_ceiling(dev, stream, gib: float, span_kib: int) -> dict:
+    """Streaming rates of hand-written probes (include/lsq_probe.h) on this GPU:
+    the best read, write and copy over a few launch shapes (one pass over the
+    buffer, 16-byte vectors, 1-4 per lane, with and without the non-temporal
+    hint), and the in-place span walk of the decode step's own access pattern
+    (one wave per span of span_kib KiB).  Best of five launches each, HIP events
+    on the launch stream; GB/s counts bytes read plus bytes written."""
+    import torch
+    import quantized_recurrent_state_amd as lsq
+
+    span = span_kib * 1024
+    nbytes = int(gib * (1 << 30)) // span * span
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(7)
+
+    def timed(fn, moved):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(5)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = min(a.elapsed_time(b) for a, b in ev)
+        return round(moved / (ms * 1e-3) / 1e9, 1)
+
+    out = {"bytes": nbytes, "method": "best of 5 launches per shape, HIP events on the launch stream"}
+    kinds = {"read": (lsq.PROBE_READ, 1), "write": (lsq.PROBE_WRITE, 1), "copy": (lsq.PROBE_COPY, 2)}
+    for name, (kind, mult) in kinds.items():
+        best = None
+        for u in (1, 2, 4):
+            for nt in (0, 1):
+                g = timed(lambda: lsq.lsq_probe_stream(kind, src, dst, nbytes, u, nt, 0, stream),
+                          mult * nbytes)
+                if best is None or g > best["gbs"]:
+                    best = {"gbs": g, "loads_per_lane": u, "nontemporal": nt, "grid": "one pass"}
+        out[name] = best
+    best = None
+    for nt in (0, 1):
+        g = timed(lambda: lsq.lsq_probe_span(src, src, nbytes, span_kib, nt, stream), 2 * nbytes)
+        if best is None or g > best["gbs"]:
+            best = {"gbs": g, "span_kib": span_kib, "nontemporal_loads": nt}
+    out["span_in_place"] = best
+    del src, dst
+    log(f"ceiling probes: {out}")
+    return out
 
 
 PREFILL_SOURCES = ("quantized_recurrent_state_amd/csrc/lsq_prefill.hip",

@@ -23,7 +23,8 @@ SCALE_F32, SCALE_F16, SCALE_BF16 = 0, 1, 2
 __all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_alloc",
            "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_dequantize", "lsq_state_set_calibrated",
            "lsq_state_step_index", "lsq_state_set_step_index",
-           "lsq_decode_step", "lsq_decode_run", "lsq_prefill", "lsq_status_string", "lsq_version"]
+           "lsq_decode_step", "lsq_decode_run", "lsq_prefill", "lsq_status_string", "lsq_version",
+           "lsq_probe_stream", "lsq_probe_span"]
 
 
 @dataclass(frozen=True)
@@ -140,6 +141,24 @@ def lsq_status_string(status: int) -> str:
 
 def lsq_version() -> int:
     return int(_lib.load().lsq_version())
+
+
+PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2
+
+
+def lsq_probe_stream(kind: int, src, dst, nbytes: int, loads_per_lane: int = 4,
+                     nontemporal: int = 0, workgroups: int = 0, stream=None) -> None:
+    """One streaming pass (include/lsq_probe.h) over device tensors src/dst."""
+    _lib.check(_lib.load().lsq_probe_stream(kind, _ptr(src), _ptr(dst), nbytes, loads_per_lane,
+                                            nontemporal, workgroups, _stream_ptr(stream)),
+               "lsq_probe_stream")
+
+
+def lsq_probe_span(src, dst, nbytes: int, span_kib: int = 10, nontemporal: int = 1,
+                   stream=None) -> None:
+    """Every wave walks its own span of src, rewriting it to dst (include/lsq_probe.h)."""
+    _lib.check(_lib.load().lsq_probe_span(_ptr(src), _ptr(dst), nbytes, span_kib, nontemporal,
+                                          _stream_ptr(stream)), "lsq_probe_span")
 
 
 class LsqState:

@@ -11,7 +11,8 @@ import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblsq.so")
-HEADER = os.path.join(os.path.dirname(_PKG), "include", "lsq.h")
+INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
+HEADER = os.path.join(INCLUDE, "lsq.h")
 
 LSQ_OK = 0
 STATUS_NAMES = {0: "LSQ_OK", 1: "LSQ_ERR_INVALID_ARG", 2: "LSQ_ERR_UNSUPPORTED",
@@ -70,6 +71,9 @@ def load() -> ctypes.CDLL:
         "lsq_status_string": [ctypes.c_int],
         "lsq_last_error": [],
         "lsq_version": [],
+        "lsq_probe_stream": [ctypes.c_int32, P, P, S, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.c_int32, P],
+        "lsq_probe_span": [P, P, S, ctypes.c_int32, ctypes.c_int32, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -88,8 +92,11 @@ def check(status: int, where: str) -> None:
         raise LsqError(status, where, detail)
 
 
-def header_functions(path: str = HEADER) -> list[str]:
-    """Names of the functions include/lsq.h declares."""
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lsq_[a-z_0-9]+)\s*\(", text)))
+def header_functions(paths: list[str] | None = None) -> list[str]:
+    """Names of the functions the headers under include/ declare."""
+    import glob
+    names = set()
+    for path in paths or sorted(glob.glob(os.path.join(INCLUDE, "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(lsq_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)

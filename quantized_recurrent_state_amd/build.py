@@ -27,8 +27,16 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
+def _headers() -> list[str]:
+    return glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        t = os.path.getmtime(obj)
+        if all(os.path.getmtime(d) < t for d in [src, __file__, *_headers()]):
+            return obj
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -36,13 +44,14 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every HIP/C++ source and link liblsq.so next to this file."""
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every HIP/C++ source and link liblsq.so next to this file
+    (incremental: skip objects newer than their source and every header)."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda x: _compile(x, incremental), srcs))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,5 +70,5 @@ def device_asm(src: str, out: str) -> None:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

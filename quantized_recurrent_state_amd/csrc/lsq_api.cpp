@@ -10,6 +10,7 @@
 
 #include "lsq.h"
 #include "lsq_internal.h"
+#include "lsq_probe.h"
 
 struct lsq_state {
   lsq_config cfg;
@@ -458,6 +459,51 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
                                      c.decay == LSQ_DECAY_DIAG, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "prefill launch");
   st->step += T;
+  return ok();
+}
+
+lsq_status lsq_probe_stream(int32_t kind, const void* src, void* dst, size_t bytes,
+                            int32_t loads_per_lane, int32_t nontemporal, int32_t workgroups,
+                            void* stream) {
+  if (kind != LSQ_PROBE_READ && kind != LSQ_PROBE_WRITE && kind != LSQ_PROBE_COPY)
+    return fail(LSQ_ERR_INVALID_ARG, "probe kind must be READ, WRITE or COPY");
+  if (bytes % 16 != 0) return fail(LSQ_ERR_INVALID_ARG, "probe size must be a multiple of 16 bytes");
+  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8)
+    return fail(LSQ_ERR_INVALID_ARG, "loads_per_lane must be 1, 2, 4 or 8");
+  if (nontemporal != 0 && nontemporal != 1)
+    return fail(LSQ_ERR_INVALID_ARG, "nontemporal must be 0 or 1");
+  if (workgroups < 0) return fail(LSQ_ERR_INVALID_ARG, "negative workgroup count");
+  if (bytes == 0) return ok();
+  if (kind != LSQ_PROBE_WRITE && (!src || !aligned16(src)))
+    return fail(LSQ_ERR_INVALID_ARG, "probe source must be non-null and 16-byte aligned");
+  if (!dst || !aligned16(dst))
+    return fail(LSQ_ERR_INVALID_ARG, "probe destination must be non-null and 16-byte aligned");
+  const size_t tile = (size_t)256 * loads_per_lane * 16;
+  if (workgroups == 0 && (bytes + tile - 1) / tile > (size_t)INT32_MAX)
+    return fail(LSQ_ERR_UNSUPPORTED, "probe size too large for a single pass");
+  hipError_t e = lsq::launch_probe(kind, src, dst, bytes, loads_per_lane, nontemporal, workgroups,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "probe launch");
+  return ok();
+}
+
+lsq_status lsq_probe_span(const void* src, void* dst, size_t bytes, int32_t span_kib,
+                          int32_t nontemporal, void* stream) {
+  if (span_kib != 1 && span_kib != 2 && span_kib != 4 && span_kib != 8 && span_kib != 10 &&
+      span_kib != 16)
+    return fail(LSQ_ERR_INVALID_ARG, "span_kib must be 1, 2, 4, 8, 10 or 16");
+  if (nontemporal != 0 && nontemporal != 1)
+    return fail(LSQ_ERR_INVALID_ARG, "nontemporal must be 0 or 1");
+  if (bytes % ((size_t)span_kib * 1024) != 0)
+    return fail(LSQ_ERR_INVALID_ARG, "probe size must be a multiple of the span");
+  if (bytes / ((size_t)span_kib * 1024) > (size_t)INT32_MAX / 4)
+    return fail(LSQ_ERR_UNSUPPORTED, "probe size too large for one launch");
+  if (bytes == 0) return ok();
+  if (!src || !dst || !aligned16(src) || !aligned16(dst))
+    return fail(LSQ_ERR_INVALID_ARG, "probe buffers must be non-null and 16-byte aligned");
+  hipError_t e = lsq::launch_probe_span(src, dst, bytes, span_kib, nontemporal,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "probe launch");
   return ok();
 }
 

@@ -112,5 +112,10 @@ hipError_t launch_head_scale(const StepArgs& a, int bits, int dk, int policy, in
 hipError_t launch_calibrate_head(const CalibArgs& a, int bits, int dk, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, int bits, int dk, hipStream_t s);
+// Streaming probe (include/lsq_probe.h): kind 0 read, 1 write, 2 copy.
+hipError_t launch_probe(int kind, const void* src, void* dst, size_t bytes, int loads_per_lane,
+                        int nontemporal, int workgroups, hipStream_t s);
+hipError_t launch_probe_span(const void* src, void* dst, size_t bytes, int span_kib, int nontemporal,
+                             hipStream_t s);
 
 }  // namespace lsq

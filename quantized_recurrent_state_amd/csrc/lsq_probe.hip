@@ -1,0 +1,148 @@
+// Device-memory streaming probe (read, write, copy) for the bandwidth
+// ceiling the decode step is measured against.  Workgroups of 256 lanes; a
+// lane moves U 16-byte vectors per iteration, issuing every load of the
+// iteration before using any; lane l of a workgroup takes vectors
+// base + u * 256 + l, so one load instruction of a wave covers 1 KiB of
+// consecutive bytes.  The grid strides over the buffer.  In span mode every
+// wave instead walks a contiguous span of its own, 1 KiB per step, reading
+// and then rewriting it (the access pattern of a decode step in which one
+// wave carries one head's packed state).
+#include <hip/hip_runtime.h>
+
+#include "lsq_internal.h"
+
+namespace lsq {
+namespace dev {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ v4u ld16(const v4u* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(v4u* p, v4u v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// KIND 0 read, 1 write, 2 copy.
+template <int KIND, int U, bool NT>
+__global__ __launch_bounds__(256) void probe_kernel(const v4u* __restrict__ src, v4u* __restrict__ dst,
+                                                     size_t n16, uint32_t* __restrict__ sink) {
+  constexpr size_t TILE = 256 * U;
+  const size_t stride = (size_t)gridDim.x * TILE;
+  size_t i = (size_t)blockIdx.x * TILE + threadIdx.x;
+  v4u acc = {0u, 0u, 0u, 0u};
+  for (; i + (U - 1) * 256 < n16; i += stride) {
+    v4u x[U];
+    if constexpr (KIND != 1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = ld16<NT>(src + i + u * 256);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (KIND == 0) {
+        acc += x[u];
+      } else if constexpr (KIND == 1) {
+        const uint32_t t = (uint32_t)(i + u * 256);
+        st16<NT>(dst + i + u * 256, v4u{t, t + 1u, t + 2u, t + 3u});
+      } else {
+        st16<NT>(dst + i + u * 256, x[u]);
+      }
+    }
+  }
+  // ragged tail: the vectors of this lane's last tile that exist
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const size_t j = i + u * 256;
+    if (j < n16) {
+      if constexpr (KIND == 0) acc += ld16<NT>(src + j);
+      else if constexpr (KIND == 1) st16<NT>(dst + j, v4u{(uint32_t)j, 0u, 0u, 0u});
+      else st16<NT>(dst + j, ld16<NT>(src + j));
+    }
+  }
+  if constexpr (KIND == 0) {
+    // keeps the loads alive; the sum of real data matching this is harmless
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = acc.x;
+  }
+}
+
+// Span mode: wave w reads the STEPS KiB at w * STEPS KiB, two steps ahead,
+// and writes each KiB back (to dst, which may equal src) with a bit flipped.
+// Compile-time step count, fully unrolled: every wait is exact.
+template <int STEPS, bool NTL>
+__global__ __launch_bounds__(256) void span_kernel(const v4u* src, v4u* dst, int nwaves) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= nwaves) return;
+  const size_t base = (size_t)wave * STEPS * 64 + lane;
+  constexpr int D = STEPS < 2 ? STEPS : 2;
+  v4u buf[STEPS];
+#pragma unroll
+  for (int d = 0; d < D; ++d) buf[d] = ld16<NTL>(src + base + d * 64);
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    if (i + D < STEPS) buf[i + D] = ld16<NTL>(src + base + (i + D) * 64);
+    v4u x = buf[i];
+    x.x ^= 1u;
+    st16<true>(dst + base + i * 64, x);
+  }
+}
+
+template <int KIND, bool NT>
+hipError_t launch_u(const void* src, void* dst, size_t n16, int u, int wg, hipStream_t s) {
+  const v4u* a = reinterpret_cast<const v4u*>(src);
+  v4u* b = reinterpret_cast<v4u*>(dst);
+  uint32_t* sink = reinterpret_cast<uint32_t*>(dst);
+  const size_t tile = 256 * (size_t)u;
+  const unsigned grid = wg > 0 ? (unsigned)wg : (unsigned)((n16 + tile - 1) / tile);
+  switch (u) {
+    case 1: hipLaunchKernelGGL((probe_kernel<KIND, 1, NT>), dim3(grid), dim3(256), 0, s, a, b, n16, sink); break;
+    case 2: hipLaunchKernelGGL((probe_kernel<KIND, 2, NT>), dim3(grid), dim3(256), 0, s, a, b, n16, sink); break;
+    case 4: hipLaunchKernelGGL((probe_kernel<KIND, 4, NT>), dim3(grid), dim3(256), 0, s, a, b, n16, sink); break;
+    case 8: hipLaunchKernelGGL((probe_kernel<KIND, 8, NT>), dim3(grid), dim3(256), 0, s, a, b, n16, sink); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dev
+
+hipError_t launch_probe_span(const void* src, void* dst, size_t bytes, int span_kib, int nontemporal,
+                             hipStream_t s) {
+  const dev::v4u* a = reinterpret_cast<const dev::v4u*>(src);
+  dev::v4u* b = reinterpret_cast<dev::v4u*>(dst);
+  const int nwaves = (int)(bytes / 1024 / span_kib);
+  if (nwaves == 0) return hipSuccess;
+  const dim3 grid((nwaves + 3) / 4), block(256);
+#define LSQ_SPAN(K)                                                                        \
+  if (span_kib == K) {                                                                     \
+    if (nontemporal)                                                                       \
+      hipLaunchKernelGGL((dev::span_kernel<K, true>), grid, block, 0, s, a, b, nwaves);    \
+    else                                                                                   \
+      hipLaunchKernelGGL((dev::span_kernel<K, false>), grid, block, 0, s, a, b, nwaves);   \
+    return hipGetLastError();                                                              \
+  }
+  LSQ_SPAN(1) LSQ_SPAN(2) LSQ_SPAN(4) LSQ_SPAN(8) LSQ_SPAN(10) LSQ_SPAN(16)
+#undef LSQ_SPAN
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_probe(int kind, const void* src, void* dst, size_t bytes, int loads_per_lane,
+                        int nontemporal, int workgroups, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const int u = loads_per_lane, wg = workgroups;
+  if (n16 == 0) return hipSuccess;
+#define LSQ_PROBE_KIND(K)                                                  \
+  if (kind == K)                                                           \
+    return nontemporal ? dev::launch_u<K, true>(src, dst, n16, u, wg, s)   \
+                       : dev::launch_u<K, false>(src, dst, n16, u, wg, s);
+  LSQ_PROBE_KIND(0)
+  LSQ_PROBE_KIND(1)
+  LSQ_PROBE_KIND(2)
+#undef LSQ_PROBE_KIND
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lsq

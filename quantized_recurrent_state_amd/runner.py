@@ -87,6 +87,16 @@ def algorithmic_bytes(cfg: LsqConfig, with_o_ref: bool = False) -> int:
     return n * (state + ins + outs + lrb)
 
 
+def state_kib_per_head(cfg: LsqConfig) -> int:
+    """Packed state of one head (codes and group scales) in KiB, rounded to a
+    span the streaming probe supports (1, 2, 4, 8, 10 or 16)."""
+    per = cfg.dv * cfg.dk * cfg.bits // 8
+    if cfg.bits != 32:
+        per += cfg.dv * (cfg.dk // cfg.group if cfg.group else 0) * (4 if cfg.scale_fmt == 0 else 2)
+    kib = per / 1024
+    return min((1, 2, 4, 8, 10, 16), key=lambda s: abs(s - kib))
+
+
 def prefill_algorithmic_bytes(cfg: LsqConfig, T: int) -> int:
     """Bytes one prefill of T tokens must move for this handle (all heads): the
     inputs k, v, alpha, beta read once, the packed codes read and written, the

@@ -218,3 +218,27 @@ def test_prefill_argument_checks_before_launch():
     assert L.lsq_prefill(h, 100, None, None, None, None, None) == 0
     assert lsq.lsq_state_step_index(h) == 100
     lsq.lsq_state_free(h)
+
+
+def test_probe_argument_checks_before_launch():
+    L = _lib.load()
+    assert L.lsq_probe_stream(3, FAKE, FAKE, 4096, 4, 0, 0, None) == 1        # kind
+    assert L.lsq_probe_stream(2, FAKE, FAKE, 4100, 4, 0, 0, None) == 1        # size % 16
+    assert L.lsq_probe_stream(2, FAKE, FAKE, 4096, 3, 0, 0, None) == 1        # loads per lane
+    assert L.lsq_probe_stream(2, FAKE, FAKE, 4096, 4, 2, 0, None) == 1        # nontemporal flag
+    assert L.lsq_probe_stream(2, FAKE, FAKE, 4096, 4, 0, -1, None) == 1       # workgroups
+    assert L.lsq_probe_stream(0, None, FAKE, 4096, 4, 0, 0, None) == 1        # read needs src
+    assert L.lsq_probe_stream(2, FAKE + 4, FAKE, 4096, 4, 0, 0, None) == 1    # misaligned
+    assert L.lsq_probe_stream(1, None, None, 4096, 4, 0, 0, None) == 1        # write needs dst
+    assert L.lsq_probe_stream(2, FAKE, FAKE, 0, 4, 0, 0, None) == 0           # empty: no-op
+    assert L.lsq_probe_stream(1, None, FAKE, 0, 1, 1, 7, None) == 0
+
+
+def test_probe_span_argument_checks_before_launch():
+    L = _lib.load()
+    assert L.lsq_probe_span(FAKE, FAKE, 10240, 3, 1, None) == 1        # span
+    assert L.lsq_probe_span(FAKE, FAKE, 10240, 10, 2, None) == 1       # nontemporal flag
+    assert L.lsq_probe_span(FAKE, FAKE, 10000, 10, 1, None) == 1       # not a whole number of spans
+    assert L.lsq_probe_span(None, FAKE, 10240, 10, 1, None) == 1       # null source
+    assert L.lsq_probe_span(FAKE, FAKE + 8, 10240, 10, 1, None) == 1   # misaligned
+    assert L.lsq_probe_span(FAKE, FAKE, 0, 10, 1, None) == 0           # empty: no-op
