@@ -28,10 +28,10 @@
  * Arithmetic contract (every step below is what the kernels compute):
  *   m_c   = fl(s_group(c) * alpha_c)            alpha_c = alpha for scalar decay
  *   S'_c  = fl(C_c * m_c)                       dequantise with the decay folded in
- *   u     = S' . k (fp32, any summation order)  only when delta = 1, else 0
+ *   u     = dot(S', k)                          only when delta = 1, else 0
  *   w     = fl(beta * fl(v_r - u))
  *   S_c   = fma(w, k_c, S'_c)
- *   o_r   = S . q (fp32, any summation order)   read before requantisation
+ *   o_r   = dot(S, q)                           read before requantisation
  *   s_new = DYNAMIC: fl(max|S_c| / qmax) per group; PERSISTENT: s;
  *           YOKED: fl(max|R_c| / qmax) with R advanced by the same update in fp32
  *   inv   = s_new == 0 ? 0 : fl(1 / s_new)
@@ -47,7 +47,14 @@
  *           sign(S_c - C_old s) (exact); B': sigma_c = sign(w) sign(k_c).  If
  *           (c1 - C_old) * sigma_c < 0 and s > 0 then c = c1 + sigma_c, else c1.
  *           On a frozen grid A never fires (it equals RNE).
- * with qmax = 2^(bits-1) - 1 (7 for INT4, 127 for INT8).
+ * with qmax = 2^(bits-1) - 1 (7 for INT4, 127 for INT8).  dot(a, b) is an
+ * fp32 sum in one fixed order (the pages leave the order open; fixing it makes
+ * every code, scale and output reproducible bit for bit): the columns are
+ * taken in consecutive blocks of 32, inside a block the products accumulate by
+ * a chain of fused multiply-adds from zero in column order, and the block sums
+ * are added in adjacent pairs, level by level ((b0 + b1) + (b2 + b3) at Dk =
+ * 128).  The unquantised mode (bits 32) keeps the same formulas with its own
+ * summation order.
  *
  * Memory: every pointer below is a DEVICE pointer (row-major, 16-byte
  * aligned) unless stated.  The library never allocates device memory: the

@@ -131,6 +131,34 @@ static double clampd(double x, double lo, double hi) { return x < lo ? lo : (x >
 
 static int sign_f(float x) { return (x > 0.0f) - (x < 0.0f); }
 
+/* A row dot product sum_c a[c] b[c] in fp32, in the one summation order this
+ * library fixes for every dot of the step (the pages leave the order open;
+ * fixing it makes the codes, which depend on the delta projection, and the
+ * outputs reproducible bit for bit): the columns are taken in consecutive
+ * blocks of 32; inside a block the products accumulate by a chain of fused
+ * multiply-adds from zero, in column order; then the block sums are added in
+ * adjacent pairs, level by level ((b0 + b1) + (b2 + b3) for four blocks; an
+ * unpaired last block passes to the next level as it is). */
+static float dot_blocked(const float* a, const float* b, int n) {
+  enum { BLOCK = 32, MAXB = 64 };
+  float part[MAXB];
+  int nb = 0;
+  for (int c0 = 0; c0 < n; c0 += BLOCK) {
+    const int c1 = (c0 + BLOCK < n) ? c0 + BLOCK : n;
+    float p = 0.0f;
+    for (int c = c0; c < c1; ++c) p = fmaf(a[c], b[c], p);
+    part[nb++] = p;
+  }
+  if (nb == 0) return 0.0f;
+  while (nb > 1) {
+    int m = 0;
+    for (int i = 0; i + 1 < nb; i += 2) part[m++] = part[i] + part[i + 1];
+    if (nb % 2) part[m++] = part[nb - 1];
+    nb = m;
+  }
+  return part[0];
+}
+
 /* Eq. (1) for one row of an fp32 state (the unquantised mode, and the yoked
  * reference).  row is updated in place; returns o_r = S_t,r . q. */
 static float fp32_row_update(const lsqo_config* cfg, float* row, const float* q, const float* k,
@@ -143,20 +171,11 @@ static float fp32_row_update(const lsqo_config* cfg, float* row, const float* q,
     scratch[c] = row[c] * a;
   }
   /* delta correction: u = S' k (the part of the state aligned with k) */
-  float u = 0.0f;
-  if (cfg->delta) {
-    double acc = 0.0;
-    for (int c = 0; c < dk; ++c) acc += (double)scratch[c] * (double)k[c];
-    u = (float)acc;
-  }
+  const float u = cfg->delta ? dot_blocked(scratch, k, dk) : 0.0f;
   /* S_t = S' (I - delta beta k k^T) + beta v k^T = S' + w k^T, w = beta (v - delta u) */
   float w = beta * (v_r - u);
-  double o = 0.0;
-  for (int c = 0; c < dk; ++c) {
-    row[c] = fmaf(w, k[c], scratch[c]);
-    o += (double)row[c] * (double)q[c];
-  }
-  return (float)o;
+  for (int c = 0; c < dk; ++c) row[c] = fmaf(w, k[c], scratch[c]);
+  return dot_blocked(row, q, dk);
 }
 
 typedef struct {
@@ -195,22 +214,15 @@ static void step_head_scale(step_job* J, int64_t h, const float* q, const float*
       const float m = s[0] * (diag ? alpha[c] : alpha[0]);
       sp[c] = (float)C[(int64_t)r * dk + c] * m;
     }
-    float u = 0.0f;
-    if (cfg->delta) {
-      double acc = 0.0;
-      for (int c = 0; c < dk; ++c) acc += (double)sp[c] * (double)k[c];
-      u = (float)acc;
-    }
+    const float u = cfg->delta ? dot_blocked(sp, k, dk) : 0.0f;
     const float w = beta * (v[r] - u);
     W[r] = w;
-    double o = 0.0;
     for (int c = 0; c < dk; ++c) {
       st[c] = fmaf(w, k[c], sp[c]);
-      o += (double)st[c] * (double)q[c];
       const float a = fabsf(st[c]);
       if (a > amax) amax = a;
     }
-    J->o[h * dv + r] = (float)o;
+    J->o[h * dv + r] = dot_blocked(st, q, dk);
   }
   const float snew = (cfg->policy == LSQO_POLICY_PERSISTENT)
                          ? s[0] : scale_as_stored(amax / (float)qm, cfg->scale_fmt);
@@ -290,19 +302,10 @@ static void step_heads(step_job* J) {
         float m = s[c / g] * a;
         sp[c] = (float)C[c] * m;
       }
-      float u = 0.0f;
-      if (cfg->delta) {
-        double acc = 0.0;
-        for (int c = 0; c < dk; ++c) acc += (double)sp[c] * (double)k[c];
-        u = (float)acc;
-      }
+      const float u = cfg->delta ? dot_blocked(sp, k, dk) : 0.0f;
       float w = beta * (v[r] - u);
-      double o = 0.0;
-      for (int c = 0; c < dk; ++c) {
-        st[c] = fmaf(w, k[c], sp[c]);
-        o += (double)st[c] * (double)q[c];
-      }
-      J->o[h * dv + r] = (float)o;
+      for (int c = 0; c < dk; ++c) st[c] = fmaf(w, k[c], sp[c]);
+      J->o[h * dv + r] = dot_blocked(st, q, dk);
 
       /* scale policy, then requantise group by group */
       for (int gi = 0; gi < ng; ++gi) {
@@ -524,8 +527,8 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
   float* sp = (float*)malloc(sizeof(float) * (size_t)dk);
   float* x = (float*)malloc(sizeof(float) * (size_t)dk);
   int* sig = (int*)malloc(sizeof(int) * (size_t)dk);
-  double* bk = (double*)malloc(sizeof(double) * (size_t)R);
-  double* bq = (double*)malloc(sizeof(double) * (size_t)R);
+  float* bk = (float*)malloc(sizeof(float) * (size_t)R);
+  float* bq = (float*)malloc(sizeof(float) * (size_t)R);
   for (int64_t h = 0; h < nh; ++h) {
     const float* qh = q + h * dk;
     const float* kh = k + h * dk;
@@ -542,16 +545,10 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
     }
     /* per-slot projections b_j . k and b_j . q */
     for (int j = 0; j < n_used; ++j) {
-      double s1 = 0.0, s2 = 0.0;
-      for (int c = 0; c < dk; ++c) {
-        s1 += (double)Bv[j * dk + c] * (double)kh[c];
-        s2 += (double)Bv[j * dk + c] * (double)qh[c];
-      }
-      bk[j] = s1;
-      bq[j] = s2;
+      bk[j] = dot_blocked(Bv + j * dk, kh, dk);
+      bq[j] = dot_blocked(Bv + j * dk, qh, dk);
     }
-    double kq = 0.0;
-    for (int c = 0; c < dk; ++c) kq += (double)kh[c] * (double)qh[c];
+    const float kq = dot_blocked(kh, qh, dk);
     /* the new slot holds k */
     for (int c = 0; c < dk; ++c) Bv[n_used * dk + c] = kh[c];
 
@@ -566,19 +563,17 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
       /* delta projection on the effective state S' + B' */
       float u = 0.0f;
       if (cfg->delta) {
-        double acc = 0.0;
-        for (int c = 0; c < dk; ++c) acc += (double)sp[c] * (double)kh[c];
-        for (int j = 0; j < n_used; ++j) acc += (double)A[j * dv + i] * bk[j];
-        u = (float)acc;
+        /* S'.k, then the slots' a_j (b_j.k) in slot order */
+        u = dot_blocked(sp, kh, dk);
+        for (int j = 0; j < n_used; ++j) u = fmaf(A[j * dv + i], bk[j], u);
       }
       const float w = beta[h] * (v[h * dv + i] - u);
       A[n_used * dv + i] = w;   /* slot n: the write w k^T */
-      /* readout from S' + B' + w k^T */
-      double oo = 0.0;
-      for (int c = 0; c < dk; ++c) oo += (double)sp[c] * (double)qh[c];
-      for (int j = 0; j < n_used; ++j) oo += (double)A[j * dv + i] * bq[j];
-      oo += (double)w * kq;
-      o[h * dv + i] = (float)oo;
+      /* readout from S' + B' + w k^T: S'.q, the slots' a_j (b_j.q), then w (k.q) */
+      float oo = dot_blocked(sp, qh, dk);
+      for (int j = 0; j < n_used; ++j) oo = fmaf(A[j * dv + i], bq[j], oo);
+      oo = fmaf(w, kq, oo);
+      o[h * dv + i] = oo;
       /* the value to requantise: the merged X on a merge step, else S' */
       for (int c = 0; c < dk; ++c) {
         float xv = sp[c], uv = 0.0f;   /* merged value, and the buffer's own value */

@@ -7,9 +7,11 @@
  *
  * The oracle is plain, slow and obviously correct: scalar loops, IEEE fp32
  * arithmetic where the method computes in fp32 (so that quantisation
- * decisions are taken in the same precision as on the GPU), double-precision
- * accumulation for the two dot products, correctly rounded fmaf from libm,
- * exact products in double for every rounding decision.
+ * decisions are taken in the same precision as on the GPU), every row dot
+ * product summed in fp32 in one stated order (blocks of 32 columns by a chain
+ * of fused multiply-adds from zero, block sums added in adjacent pairs; the
+ * pages leave the order open and this fixes it), correctly rounded fmaf from
+ * libm, exact products in double for every rounding decision.
  *
  * Sources (page title, then the passage):
  *  - "LinQuant: Functional Invariances for Low-Precision Linear Recurrences"

@@ -3,10 +3,10 @@
 Teacher-forced as the plain step (tests/parity.py): before every step the
 oracle takes the GPU's codes, scales and bypass slots (a, and the b copy the
 step reads); after it the codes, scales and o are held to the usual bar, and
-the slots the next step will read are compared: decayed slots and the new
-b = k bit for bit, the new a = w (which depends on the delta projection's
-summation order) within 1e-5 of its row's norm.  Runs of 2r+1 steps cover
-two merges and the slot reuse after a merge.
+the slots the next step will read are compared bit for bit: decayed slots, the
+new b = k and the new a = w (the delta projection is summed in the one order
+both sides fix).  Runs of 2r+1 steps cover two merges and the slot reuse after
+a merge.
 """
 import numpy as np
 import pytest
@@ -15,7 +15,7 @@ import torch
 import oracle
 import quantized_recurrent_state_amd as lsq
 from quantized_recurrent_state_amd.inputs import gen_steps
-from tests.parity import Report, compare_step, ocfg_of, snapshot, _normwise
+from tests.parity import Report, compare_step, ocfg_of, snapshot
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -57,7 +57,7 @@ def _run(cfg, steps, recipe, t0=0, edit=None):
             used = n_after - 1                     # slots decayed this step
             assert np.array_equal(ga[:, :used], want.lrb_a[:, :used]), (t, "decayed a")
             assert np.array_equal(gb[:, :n_after], want.lrb_b[:, :n_after]), (t, "b")
-            assert _normwise(ga[:, used], want.lrb_a[:, used]) <= 1e-5, (t, "new a")
+            assert np.array_equal(ga[:, used], want.lrb_a[:, used]), (t, "new a")
     return rep
 
 
@@ -79,7 +79,7 @@ def test_bypass_step_matches_oracle(bits, dk, pol, rnd, dl, dc):
     rep = _run(cfg, 2 * R + 1, recipe)
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
-    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)
 
 
 @pytest.mark.parametrize("R", [1, 2, 8])
@@ -106,7 +106,7 @@ def test_bypass_merge_without_update_direction(bits, pol, dl, dc):
     rep = _run(cfg, 2 * R + 1, recipe, edit=lambda d: zero_directions(d, 128))
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
-    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)
 
 
 @pytest.mark.parametrize("R,bits,pol,rnd,dc", [
@@ -122,4 +122,4 @@ def test_bypass_large_ranks(R, bits, pol, rnd, dc):
     rep = _run(cfg, R + 2, "gla" if dc == lsq.DECAY_DIAG else "gdn", t0=2 * R - 1)
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
-    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)

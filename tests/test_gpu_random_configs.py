@@ -58,8 +58,7 @@ def test_random_configuration(seed):
     rep = _run_teacher_forced(cfg, steps=4, recipe=recipe)
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
-    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
-    assert rep.excused_groups <= max(2, rep.groups // 100), str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)
 
 
 def _draw_bypass(seed):
@@ -84,4 +83,4 @@ def test_random_bypass_configuration(seed):
     rep = test_gpu_lrb._run(cfg, 2 * cfg.lrb_rank + 1, recipe, t0=t0)
     print(f"\n{cfg}: {rep}")
     assert rep.ok, str(rep)
-    assert rep.excused <= max(2, rep.codes // 20000), str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)
