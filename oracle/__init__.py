@@ -16,6 +16,7 @@ of the quantiser.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -69,30 +70,65 @@ def lib():
     global _lib
     with _lib_lock:
         if _lib is None:
-            L = ctypes.CDLL(build())
-            P = ctypes.c_void_p
-            cfgp = ctypes.POINTER(_Config)
-            L.lsqo_check_config.argtypes = [cfgp]
-            L.lsqo_step.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(_Stats)]
-            L.lsqo_step_trace.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P, P,
-                                          ctypes.POINTER(_Stats), P, P]
-            L.lsqo_run.argtypes = [cfgp, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
-                                   ctypes.c_int32]
-            L.lsqo_calibrate.argtypes = [cfgp, P, P, P, P, P]
-            L.lsqo_step_lrb.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P,
-                                        ctypes.POINTER(_Stats), P, P]
-            L.lsqo_prefill.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P]
-            L.lsqo_dequantize.argtypes = [cfgp, P, P, P]
-            L.lsqo_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
-            L.lsqo_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
-            for f in (L.lsqo_check_config, L.lsqo_step, L.lsqo_step_trace, L.lsqo_run, L.lsqo_calibrate,
-                      L.lsqo_step_lrb, L.lsqo_prefill,
-                      L.lsqo_dequantize, L.lsqo_pack, L.lsqo_unpack):
-                f.restype = ctypes.c_int
-            L.lsqo_scale_as_stored.argtypes = [ctypes.c_float, ctypes.c_int32]
-            L.lsqo_scale_as_stored.restype = ctypes.c_float
-            _lib = L
+            _lib = _load(build())
         return _lib
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    cfgp = ctypes.POINTER(_Config)
+    L.lsqo_check_config.argtypes = [cfgp]
+    L.lsqo_step.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(_Stats)]
+    L.lsqo_step_trace.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P, P,
+                                  ctypes.POINTER(_Stats), P, P]
+    L.lsqo_run.argtypes = [cfgp, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P, P,
+                           ctypes.c_int32]
+    L.lsqo_calibrate.argtypes = [cfgp, P, P, P, P, P]
+    L.lsqo_step_lrb.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, P,
+                                ctypes.POINTER(_Stats), P, P]
+    L.lsqo_prefill.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P]
+    L.lsqo_dequantize.argtypes = [cfgp, P, P, P]
+    L.lsqo_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
+    L.lsqo_unpack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P]
+    for f in (L.lsqo_check_config, L.lsqo_step, L.lsqo_step_trace, L.lsqo_run, L.lsqo_calibrate,
+              L.lsqo_step_lrb, L.lsqo_prefill,
+              L.lsqo_dequantize, L.lsqo_pack, L.lsqo_unpack):
+        f.restype = ctypes.c_int
+    L.lsqo_scale_as_stored.argtypes = [ctypes.c_float, ctypes.c_int32]
+    L.lsqo_scale_as_stored.restype = ctypes.c_float
+    return L
+
+
+@contextlib.contextmanager
+def planted(edits):
+    """TEST SUPPORT: inside the block every function of this module runs an
+    oracle built from lsq_oracle.c with the given (old, new) source edits
+    applied: a planted mistake, compiled on the CPU into a temporary
+    directory, to show that a pin catches it.  Each old text must occur in the
+    source exactly once."""
+    global _lib
+    import tempfile
+    text = open(_SRC).read()
+    for old, new in edits:
+        if text.count(old) != 1:
+            raise ValueError(f"planted edit does not match exactly once: {old!r}")
+        text = text.replace(old, new)
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "lsq_oracle.c")
+        with open(src, "w") as f:
+            f.write(text)
+        out = os.path.join(d, "liblsq_oracle_planted.so")
+        subprocess.run(["gcc", *GCC_FLAGS, f"-I{_HERE}", "-o", out, src, "-lm", "-pthread"],
+                       check=True)
+        keep = lib()
+        with _lib_lock:
+            _lib = _load(out)
+        try:
+            yield
+        finally:
+            with _lib_lock:
+                _lib = keep
 
 
 @dataclass(frozen=True)
