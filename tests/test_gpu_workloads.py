@@ -10,10 +10,11 @@ inputs), on sampled heads compared teacher-forced with the CPU oracle.
   mamba2   8192 heads, Dv 64, INT8 g64 persistent, BDR vs RNE: 4096 steps,
            checked at sampled steps
   stack24  393216 heads in two launches (INT8 g64 layers 0-3, INT4 g32 layers
-           4-23), persistent, BDR: warmup, calibration and the first steps; the
-           same for the stack's variants the benchmark runs (RNE, Weyl dither,
-           16-element groups, bfloat16 scales, one scale per head, reading B'),
-           and for Gated DeltaNet with a dynamic scale per head
+           4-23), persistent, BDR: warmup, calibration and the whole 32768-step
+           horizon checked at sampled steps (the first four, every 4096th, the
+           last); the first steps of the stack's variants the benchmark runs
+           (RNE, Weyl dither, 16-element groups, bfloat16 scales, one scale per
+           head, reading B'), and of Gated DeltaNet with a dynamic scale per head
 """
 import numpy as np
 import pytest
@@ -42,9 +43,11 @@ def _check_calibration(st, S_W, sel):
     assert np.array_equal(got.scales, want.scales)
 
 
-def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64):
+def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64, per_step=None,
+                 progress=0):
     """Step every arm through `steps` steps; at the steps in check_steps compare
-    the sampled heads teacher-forced.  Returns one Report per arm."""
+    the sampled heads teacher-forced.  Returns one Report per arm; per_step, if
+    given, collects (step, arm index, Report) of every check."""
     reps = [Report() for _ in arms_state]
     sels = [_sample(st.cfg.n, sel_n) for st in arms_state]
     npl = wl.batch * wl.heads
@@ -81,10 +84,15 @@ def _run_checked(wl, arms_state, t_first, steps, check_steps, sel_n, chunk=64):
                                 for x in ("q", "k", "v", "alpha", "beta"))
                     ocfg = ocfg_of(st.cfg, step=step_index).replace(batch=len(sel), heads=1,
                                                                     lrb_rank=st.cfg.lrb_rank)
-                    reps[ai].add(compare_step(
+                    r1 = compare_step(
                         ocfg, before, inp, after, o.index_select(0, sel).cpu().numpy(),
-                        None if o_ref is None else o_ref.index_select(0, sel).cpu().numpy()))
+                        None if o_ref is None else o_ref.index_select(0, sel).cpu().numpy())
+                    reps[ai].add(r1)
+                    if per_step is not None:
+                        per_step.append((t, ai, r1))
         del inputs
+        if progress and (c0 + nc) // progress != c0 // progress:
+            print(f"{wl.name}: {c0 + nc} of {steps} steps", flush=True)
     return reps
 
 
@@ -138,6 +146,31 @@ def test_mamba2_bdr_vs_rne():
     _assert_ok(wl, reps)
     # the two arms ran on identical inputs from identical calibrated states
     assert reps[0].bdr_fired > 0 and reps[1].bdr_fired == 0
+
+
+@pytest.mark.timeout(1200)
+def test_stack24_whole_horizon():
+    """The 24-layer stack (393 216 heads, INT8 g64 layers 0-3 and INT4 g32 layers
+    4-23, persistent scales, BDR, delta rule) through all 32 768 quantised steps
+    after its 64-step fp32 warmup, in the benchmark's launch configuration:
+    teacher-forced on 48 sampled heads per arm at steps 0-3, every 4096th step
+    and the last one; clamp and directional-rounding rates reported along the
+    horizon ("When Dynamic Scaling Fails", abstract: group-wise INT4 run out to
+    32K)."""
+    wl = WORKLOADS["stack24"]
+    states, t0 = _prepare(wl, sel_n=48)
+    checks = set(range(4)) | set(range(4095, wl.steps, 4096)) | {wl.steps - 1}
+    per_step = []
+    reps = _run_checked(wl, states, t0, wl.steps, checks, sel_n=48, chunk=32, per_step=per_step,
+                        progress=4096)
+    for t, ai, r1 in per_step:
+        n = max(1, r1.codes)
+        print(f"step {t:5d} {wl.arms[ai].name}: clamp rate {r1.clamped / n:.5f} "
+              f"directional-rounding rate {r1.bdr_fired / n:.5f} {'ok' if r1.ok else 'FAIL'}")
+    assert {t for t, _, _ in per_step} == checks
+    _assert_ok(wl, reps)
+    del states
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("key", ["stack24", "stack24-rne", "stack24-dither", "stack24-g16",
