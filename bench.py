@@ -61,6 +61,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=8,
+                    help="steps per lsq_decode_run call in the timed region")
     ap.add_argument("--workload", default="stack24")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
@@ -105,7 +107,7 @@ def main() -> int:
         if wl.shared_inputs and shared is not None:
             inp = shared
         else:
-            inp = runner.inputs(wl, arm, t_first, W + K + (K if args.graph else 0), npl, dev)
+            inp = runner.inputs(wl, arm, t_first, W + 2 * K + (K if args.graph else 0), npl, dev)
             if wl.shared_inputs:
                 shared = inp
         o = torch.empty((cfg.n, cfg.dv), device=dev)
@@ -127,19 +129,39 @@ def main() -> int:
             launch(a, t)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, events around every launch of the dominant kernel
-    # events around every launch of every arm, on the launch stream
+    # ---- timed region: K steps through lsq_decode_run, in chunks of C steps per arm
+    # (the library's horizon driver; the wall clock includes the launch gaps)
+    C = max(1, min(args.chunk, K))
+
+    def run_chunk(a, t, h, s=stream):
+        i = a["inp"]
+        lsq.lsq_decode_run(a["st"].handle, h, i["q"][t:t + h], i["k"][t:t + h], i["v"][t:t + h],
+                           i["alpha"][t:t + h], i["beta"][t:t + h], a["o_run"][:h],
+                           None if a["o_ref"] is None else a["o_ref_run"][:h], s)
+
+    for a in arms:
+        a["o_run"] = torch.empty((C, a["cfg"].n, a["cfg"].dv), device=dev)
+        a["o_ref_run"] = torch.empty_like(a["o_run"]) if a["o_ref"] is not None else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c0 in range(W, W + K, C):
+        h = min(C, W + K - c0)
+        for a in arms:
+            run_chunk(a, c0, h)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # ---- kernel time per launch: the next K steps one launch at a time, HIP events
+    # around every launch on the launch stream (outside the wall-clock region)
     ev_s = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in arms]
     ev_e = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in arms]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j, t in enumerate(range(W, W + K)):
+    for j, t in enumerate(range(W + K, W + 2 * K)):
         for i, a in enumerate(arms):
             ev_s[i][j].record(stream)
             launch(a, t)
             ev_e[i][j].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     for i, a in enumerate(arms):
         ms = sorted(x.elapsed_time(y) for x, y in zip(ev_s[i], ev_e[i]))
         a["launch_us"] = {"median": round(ms[len(ms) // 2] * 1e3, 2),
@@ -155,8 +177,8 @@ def main() -> int:
     gbs = bytes_step * K / wall / 1e9
     dom_a = arms[dom]
     dom_gbs = dom_a["bytes"] / (kern_ms_mean * 1e-3) / 1e9
-    log(f"timed {K} steps: {wall * 1e3 / K:.3f} ms/step, {gbs:.1f} GB/s; dominant kernel "
-        f"{kern_ms_mean * 1e3:.1f} us, {dom_gbs:.1f} GB/s")
+    log(f"timed {K} steps (lsq_decode_run, chunks of {C}): {wall * 1e3 / K:.3f} ms/step, "
+        f"{gbs:.1f} GB/s; dominant kernel {kern_ms_mean * 1e3:.1f} us, {dom_gbs:.1f} GB/s")
 
     # ---- optional: the next K steps captured in one HIP graph and replayed once
     # (every launch records its own inputs, step index and bypass slot at
@@ -167,7 +189,7 @@ def main() -> int:
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream()
-            for t in range(W + K, W + 2 * K):
+            for t in range(W + 2 * K, W + 3 * K):
                 for a in arms:
                     launch(a, t, cs)
         torch.cuda.synchronize()
@@ -211,7 +233,7 @@ def main() -> int:
             f = lsq.LsqState(runner.fp32_config(a["cfg"]), device=dev).zero()
             fl.append((a, f))
         torch.cuda.synchronize()
-        nf = min(args.fp32_steps, W + K)
+        nf = min(args.fp32_steps, W + 2 * K)
         tf0 = time.perf_counter()
         for t in range(nf):
             for a, f in fl:
@@ -249,7 +271,7 @@ def main() -> int:
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(arms, args.cpu_seconds, W + K)
+        cpu = cpu_baseline(arms, args.cpu_seconds, W + 2 * K)
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -448,7 +470,7 @@ def cpu_baseline_prefill(wl, cfg, st, inp, seconds: float, nbytes: int):
     import oracle
     from tests.parity import ocfg_of, snapshot
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, host_cores, _ = host_threads()
     n = cfg.n
 
     def sample(m):
@@ -479,25 +501,38 @@ def cpu_baseline_prefill(wl, cfg, st, inp, seconds: float, nbytes: int):
     dt = run(m)
     log(f"cpu oracle prefill: {m} sampled heads x {wl.tokens} tokens in {dt:.1f} s on {threads} threads")
     return {"value": round(nbytes * m / n / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "tokens_per_s": round(m * wl.tokens / dt, 1),
+            "host_cores": host_cores, "kind": "oracle", "tokens_per_s": round(m * wl.tokens / dt, 1),
             "sample": f"{m} of {n} heads (evenly spaced) x the full {wl.tokens}-token prompt, "
                       f"from the GPU's state, on the same inputs"}
 
 
+def host_threads() -> tuple[int, int, int]:
+    """(threads the CPU baseline uses, host cores, cores this process may run on).
+    The oracle runs one worker per available core up to 16, the CPU share of
+    one GPU on the machines this benchmark targets."""
+    host = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = host
+    return max(1, min(16, avail)), host, avail
+
+
 def cpu_baseline(arms, seconds: float, steps_avail: int):
-    """Time the CPU oracle on sampled heads of every arm (same inputs and state
-    as the GPU), scaled to the benchmark's unit."""
+    """Time the CPU oracle on every arm of the workload (same inputs and state as
+    the GPU), scaled to the benchmark's unit: all heads and all the steps that
+    fit the time budget when the workload is small, else evenly spaced heads;
+    with every available worker thread and with one thread."""
     import numpy as np
     import oracle
     from quantized_recurrent_state_amd import runner
     from tests.parity import ocfg_of, snapshot
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    frac = 1.0 / 32                               # sampled share of every arm's heads
-    samples = []
-    for a in arms:
+    threads, host_cores, avail = host_threads()
+    per_arm = seconds / max(1, len(arms))
+
+    def sample(a, m):
         n = a["cfg"].n
-        m = max(threads, int(n * frac))
         idx = np.linspace(0, n - 1, m).astype(np.int64)
         sel = __import__("torch").as_tensor(idx, device=a["st"].device)
         st = snapshot(a["st"], heads=sel)
@@ -507,59 +542,72 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
             cin = (t_now & 1) if a["cfg"].decay else 0
             st.lrb_a = a["st"].lrb_a.index_select(0, sel).cpu().numpy().copy()
             st.lrb_b = a["st"].lrb_b[:, cin].index_select(0, sel).cpu().numpy().copy()
-        samples.append((a, ocfg, st, sel))
+        return ocfg, st, sel
 
-    def run(steps):
-        total_b, total_hs, dt = 0, 0, 0.0
-        for a, ocfg, st, sel in samples:
-            i = a["inp"]
-            x = {k: i[k][:steps].index_select(1, sel).cpu().numpy() for k in i}
-            s2 = st.copy()
-            t0 = time.perf_counter()
-            if ocfg.lrb_rank > 0:
-                # the bypass oracle steps one call at a time: split the sampled heads
-                # over threads (the oracle releases the interpreter while it runs)
-                import concurrent.futures as cf
-                bounds = np.linspace(0, ocfg.n, threads + 1).astype(np.int64)
+    def timed(a, ocfg, st, sel, steps, nthr):
+        i = a["inp"]
+        x = {k: i[k][:steps].index_select(1, sel).cpu().numpy() for k in i}
+        s2 = st.copy()
+        t0 = time.perf_counter()
+        if ocfg.lrb_rank > 0:
+            # the bypass oracle steps one call at a time: split the heads over
+            # threads (the oracle releases the interpreter while it runs)
+            import concurrent.futures as cf
+            bounds = np.linspace(0, ocfg.n, nthr + 1).astype(np.int64)
 
-                def part(lo, hi):
-                    sub = oracle.OracleState(codes=s2.codes[lo:hi], scales=s2.scales[lo:hi],
-                                             lrb_a=s2.lrb_a[lo:hi], lrb_b=s2.lrb_b[lo:hi])
-                    c = ocfg.replace(batch=int(hi - lo))
-                    for t in range(steps):
-                        oracle.step(c.replace(step=ocfg.step + t), sub, x["q"][t][lo:hi],
-                                    x["k"][t][lo:hi], x["v"][t][lo:hi], x["alpha"][t][lo:hi],
-                                    x["beta"][t][lo:hi])
+            def part(lo, hi):
+                sub = oracle.OracleState(codes=s2.codes[lo:hi], scales=s2.scales[lo:hi],
+                                         lrb_a=s2.lrb_a[lo:hi], lrb_b=s2.lrb_b[lo:hi])
+                c = ocfg.replace(batch=int(hi - lo))
+                for t in range(steps):
+                    oracle.step(c.replace(step=ocfg.step + t), sub, x["q"][t][lo:hi],
+                                x["k"][t][lo:hi], x["v"][t][lo:hi], x["alpha"][t][lo:hi],
+                                x["beta"][t][lo:hi])
 
-                with cf.ThreadPoolExecutor(threads) as ex:
-                    list(ex.map(lambda i: part(bounds[i], bounds[i + 1]), range(threads)))
-            else:
-                oracle.run(ocfg, s2, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
-                           nthreads=threads)
-            dt += time.perf_counter() - t0
-            total_b += runner.algorithmic_bytes(a["cfg"]) // a["cfg"].n * ocfg.n * steps
-            total_hs += ocfg.n * steps
-        return total_b, total_hs, dt
+            with cf.ThreadPoolExecutor(nthr) as ex:
+                list(ex.map(lambda j: part(bounds[j], bounds[j + 1]), range(nthr)))
+        else:
+            oracle.run(ocfg, s2, x["q"], x["k"], x["v"], x["alpha"], x["beta"], nthreads=nthr)
+        return time.perf_counter() - t0
 
-    _, _, dt1 = run(1)
-    steps = int(max(1, min(steps_avail, round(seconds / max(dt1, 1e-3)))))
-    b, hs, dt = run(steps)
-    heads = sum(o.n for _, o, _, _ in samples)
-    log(f"cpu oracle: {heads} sampled heads x {steps} steps in {dt:.1f} s on {threads} threads")
-    # one core, one step of the first arm's sample; and the rounding statistics
-    # of one oracle step on every arm's sample (element-steps changed by
-    # directional rounding, and clamped at qmax)
-    a0, o0, s0, sel0 = samples[0]
-    x0 = {k: a0["inp"][k][:1].index_select(1, sel0).cpu().numpy() for k in a0["inp"]}
-    one_core = None
-    if o0.lrb_rank == 0:
-        t1 = time.perf_counter()
-        oracle.run(o0, s0.copy(), x0["q"], x0["k"], x0["v"], x0["alpha"], x0["beta"], nthreads=1)
-        dt_one = time.perf_counter() - t1
-        one_core = round(runner.algorithmic_bytes(a0["cfg"]) // a0["cfg"].n * o0.n / dt_one / 1e9, 4)
+    results, tot_b, tot_hs, tot_dt, tot_b1, tot_dt1 = [], 0, 0, 0.0, 0, 0.0
+    for a in arms:
+        n = a["cfg"].n
+        bph = runner.algorithmic_bytes(a["cfg"]) // n          # bytes per head-step
+        # the rate of one step on `threads` heads sets the sample size
+        ocfg, st, sel = sample(a, min(n, threads))
+        dt0 = max(timed(a, ocfg, st, sel, 1, threads), 1e-4)
+        per_hs = dt0 / ocfg.n * threads                        # seconds per head-step, one thread
+        budget = per_arm * threads / per_hs                    # head-steps that fit the budget
+        if n * steps_avail <= budget:
+            m, steps = n, steps_avail                          # the whole workload as timed
+        else:
+            steps = int(max(1, min(steps_avail, budget // min(n, max(threads, n // 32)))))
+            m = int(max(threads, min(n, budget // steps)))
+        ocfg, st, sel = sample(a, m)
+        dt = timed(a, ocfg, st, sel, steps, threads)
+        # one thread on a share of the same sample (1/threads of the heads)
+        m1 = max(1, m // threads)
+        o1, s1, sel1 = sample(a, m1)
+        dt1 = timed(a, o1, s1, sel1, steps, 1)
+        results.append({"arm": a["arm"].name, "heads": m, "of_heads": n, "steps": steps,
+                        "gbs": round(bph * m * steps / dt / 1e9, 4),
+                        "head_steps_per_s": round(m * steps / dt, 1),
+                        "gbs_one_thread": round(bph * m1 * steps / dt1 / 1e9, 4),
+                        "head_steps_per_s_one_thread": round(m1 * steps / dt1, 1)})
+        tot_b += bph * m * steps
+        tot_hs += m * steps
+        tot_dt += dt
+        tot_b1 += bph * m1 * steps
+        tot_dt1 += dt1
+        log(f"cpu oracle, {a['arm'].name}: {m} of {n} heads x {steps} steps in {dt:.1f} s on "
+            f"{threads} threads; {m1} heads in {dt1:.1f} s on one thread")
+    # rounding statistics of one oracle step (a whole merge period for the bypass)
+    # on up to 64 heads of every arm: element-steps changed by directional
+    # rounding, and clamped at qmax
     rates = []
-    for a, ocfg, st, sel in samples:
-        # one step, or a whole merge period of the bypass (its rounding acts at the merge)
+    for a in arms:
+        ocfg, st, sel = sample(a, min(a["cfg"].n, 64))
         nst = max(1, ocfg.lrb_rank)
         s2, fired, clamped = st.copy(), 0, 0
         for t in range(nst):
@@ -572,11 +620,18 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
         ne = ocfg.n * ocfg.dv * ocfg.dk * nst
         rates.append({"arm": a["arm"].name, "steps": nst, "bdr_fired_rate": round(fired / ne, 5),
                       "clamp_rate": round(clamped / ne, 5)})
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "value_one_core": one_core, "rounding_stats": rates,
-            "head_steps_per_s": round(hs / dt, 1),
-            "sample": f"{heads} heads (1/32 of every arm, evenly spaced) x {steps} steps of the "
-                      f"same workload, from the GPU's state, on the same inputs"}
+    whole = all(r["heads"] == r["of_heads"] and r["steps"] == steps_avail for r in results)
+    return {"value": round(tot_b / tot_dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "host_cores": host_cores, "cores_available": avail, "kind": "oracle",
+            "value_one_thread": round(tot_b1 / tot_dt1 / 1e9, 4),
+            "head_steps_per_s": round(tot_hs / tot_dt, 1), "arms": results,
+            "rounding_stats": rates,
+            "sample": ("the whole workload as the GPU timed it" if whole else
+                       "evenly spaced heads of every arm x the steps that fit about "
+                       f"{per_arm:.0f} s per arm") +
+                      f"; from the GPU's state, on the same inputs; {threads} worker threads "
+                      "(one per available core, at most 16), and one thread on 1/"
+                      f"{threads} of the heads"}
 
 
 if __name__ == "__main__":
