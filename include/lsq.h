@@ -242,16 +242,48 @@ lsq_status lsq_state_set_calibrated(lsq_state* st, int32_t calibrated);
 lsq_status lsq_state_step_index(const lsq_state* st, int64_t* t);
 lsq_status lsq_state_set_step_index(lsq_state* st, int64_t t);
 
-/* One decode step for all heads (shapes above).  alpha has [heads] or
+/* One decode step for all heads (shapes above): Eq. (1) of "LinQuant:
+ * Functional Invariances for Low-Precision Linear Recurrences" (Theoretical
+ * Foundation) applied to the dequantised state, the output read from the
+ * updated fp32 state, and the state requantised under the handle's scale
+ * policy and rounding, as "When Dynamic Scaling Fails" (abstract) describes
+ * the per-token requantisation of the decode step; the arithmetic contract at
+ * the top of this file states every operation.  alpha has [heads] or
  * [heads][Dk] entries by the decay flag.  o_ref may be NULL; it is written
- * only by the yoked policy.  The state is updated in place. */
+ * only by the yoked policy.  The state is updated in place and the handle's
+ * step index advances by one.
+ *
+ * Ownership and errors: every pointer is a device pointer the caller owns;
+ * nothing is retained after the call returns (the launch is asynchronous on
+ * stream).  INVALID_ARG for a null handle or data pointer, or one that is not
+ * 16-byte aligned (q, k, a diagonal alpha) or 4-byte aligned (v, a scalar
+ * alpha, beta, o); NOT_CALIBRATED for a persistent-policy handle that was never
+ * calibrated; HIP for a launch failure.
+ *
+ * HIP graphs: the launch allocates nothing and records no memset, so it can be
+ * captured.  The step index, and with it the dither's sequence positions, the
+ * bypass slot that is filled and which of the two b copies is read, is taken
+ * from the handle on the host when the launch is issued: a captured launch
+ * keeps the values of the step it was captured at.  Replaying a captured
+ * sequence therefore redoes those same steps (same positions, same slots); to
+ * advance a decode with a graph, capture as many steps as one replay should
+ * take and, for the bypass, a whole number of merge periods starting at a
+ * period boundary, and set the handle's step index (lsq_state_set_step_index)
+ * to what the replays have reached before issuing further uncaptured steps. */
 lsq_status lsq_decode_step(lsq_state* st, const float* q, const float* k, const float* v,
                            const float* alpha, const float* beta, float* o, float* o_ref,
                            void* stream);
 
-/* H sequential decode steps ("decode horizon H"); every input carries a
- * leading [H] axis (contiguous, step-major), o (and o_ref) receive
- * [H][heads][Dv].  The state round-trips through device memory every step. */
+/* H sequential decode steps over a decode horizon H: the state is rewritten
+ * and requantised at every step of the horizon ("When Dynamic Scaling Fails",
+ * abstract: the requantisation happens per token, and its effect is measured
+ * against the horizon H), each step exactly lsq_decode_step.  Every input
+ * carries a leading [H] axis (contiguous, step-major), o (and o_ref) receive
+ * [H][heads][Dv].  The state round-trips through device memory every step; H
+ * kernel launches are issued on stream; the step index advances by H.  H = 0
+ * or no heads: nothing is launched.  Errors as lsq_decode_step (a negative H
+ * is INVALID_ARG); a launch failure part-way returns HIP with the earlier
+ * steps issued. */
 lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float* k,
                           const float* v, const float* alpha, const float* beta, float* o,
                           float* o_ref, void* stream);
