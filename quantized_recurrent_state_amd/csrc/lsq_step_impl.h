@@ -207,31 +207,42 @@ struct Fmt {
   static constexpr float MQ = kMagic + BIAS;                    // rounding constant, offset built in
 };
 
-// Offset-binary code words -> unsigned code values (element order = column order).
+// Offset-binary code words -> unsigned code values (element order = column
+// order), for one block of eight elements: wb holds its words (one INT4 word,
+// two INT8 words).
 template <int BITS>
-__device__ __forceinline__ void unpack_offsets(const uint32_t (&xo)[Fmt<BITS>::NW], float (&f)[EPL]) {
+__device__ __forceinline__ void unpack_block(const uint32_t* wb, float (&f)[8]) {
   if constexpr (BITS == 4) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = and_opaque(xo[j], 0x0F0F0F0Fu);          // even columns, one per byte
-      const uint32_t hi = and_opaque(xo[j] >> 4, 0x0F0F0F0Fu);     // odd columns
-      f[8 * j + 0] = static_cast<float>(lo & 0xFFu);
-      f[8 * j + 1] = static_cast<float>(hi & 0xFFu);
-      f[8 * j + 2] = static_cast<float>((lo >> 8) & 0xFFu);
-      f[8 * j + 3] = static_cast<float>((hi >> 8) & 0xFFu);
-      f[8 * j + 4] = static_cast<float>((lo >> 16) & 0xFFu);
-      f[8 * j + 5] = static_cast<float>((hi >> 16) & 0xFFu);
-      f[8 * j + 6] = static_cast<float>(lo >> 24);
-      f[8 * j + 7] = static_cast<float>(hi >> 24);
-    }
+    const uint32_t lo = and_opaque(wb[0], 0x0F0F0F0Fu);          // even columns, one per byte
+    const uint32_t hi = and_opaque(wb[0] >> 4, 0x0F0F0F0Fu);     // odd columns
+    f[0] = static_cast<float>(lo & 0xFFu);
+    f[1] = static_cast<float>(hi & 0xFFu);
+    f[2] = static_cast<float>((lo >> 8) & 0xFFu);
+    f[3] = static_cast<float>((hi >> 8) & 0xFFu);
+    f[4] = static_cast<float>((lo >> 16) & 0xFFu);
+    f[5] = static_cast<float>((hi >> 16) & 0xFFu);
+    f[6] = static_cast<float>(lo >> 24);
+    f[7] = static_cast<float>(hi >> 24);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f[4 * j + 0] = static_cast<float>(xo[j] & 0xFFu);
-      f[4 * j + 1] = static_cast<float>((xo[j] >> 8) & 0xFFu);
-      f[4 * j + 2] = static_cast<float>((xo[j] >> 16) & 0xFFu);
-      f[4 * j + 3] = static_cast<float>(xo[j] >> 24);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t x = wb[h];
+      f[4 * h + 0] = static_cast<float>(x & 0xFFu);
+      f[4 * h + 1] = static_cast<float>((x >> 8) & 0xFFu);
+      f[4 * h + 2] = static_cast<float>((x >> 16) & 0xFFu);
+      f[4 * h + 3] = static_cast<float>(x >> 24);
     }
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void unpack_offsets(const uint32_t (&xo)[Fmt<BITS>::NW], float (&f)[EPL]) {
+#pragma unroll
+  for (int b = 0; b < EPL / 8; ++b) {
+    float t[8];
+    unpack_block<BITS>(&xo[b * (BITS == 4 ? 1 : 2)], t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[8 * b + i] = t[i];
   }
 }
 
@@ -253,44 +264,53 @@ __device__ __forceinline__ float fma_mix(uint32_t h, float b, float c) {
 // a separate int -> float conversion: two codes at a time are masked into the
 // low bits of the two halves of a word (binary16 subnormals u * 2^-24, or
 // 16u * 2^-24 for INT4 high nibbles) and v_fma_mix_f32 multiplies them by
-// m * 2^24 (resp. m * 2^20), both exact scalings of m.
-// With two groups per lane (GPL = 2, 16-element groups) elements 0-15 take
-// m[0] and elements 16-31 m[1].
+// m * 2^24 (resp. m * 2^20), both exact scalings of m.  One block of eight
+// elements (wb: its words) with the block's multiplier m and bias product mb.
+template <int BITS>
+__device__ __forceinline__ void dequant_mix_block(const uint32_t* wb, float m, float mb,
+                                                  float (&f)[8]) {
+  if constexpr (BITS == 4) {
+    const float m24 = m * 0x1p24f, m20 = m * 0x1p20f;
+    const uint32_t x = wb[0];
+    const uint32_t a = x & 0x000F000Fu;          // columns 8b, 8b+4
+    const uint32_t bb = x & 0x00F000F0u;         // columns 8b+1, 8b+5 (times 16)
+    const uint32_t c = (x >> 8) & 0x000F000Fu;   // columns 8b+2, 8b+6
+    const uint32_t d = (x >> 8) & 0x00F000F0u;   // columns 8b+3, 8b+7 (times 16)
+    f[0] = fma_mix<false>(a, m24, mb);
+    f[4] = fma_mix<true>(a, m24, mb);
+    f[1] = fma_mix<false>(bb, m20, mb);
+    f[5] = fma_mix<true>(bb, m20, mb);
+    f[2] = fma_mix<false>(c, m24, mb);
+    f[6] = fma_mix<true>(c, m24, mb);
+    f[3] = fma_mix<false>(d, m20, mb);
+    f[7] = fma_mix<true>(d, m20, mb);
+  } else {
+    const float m24 = m * 0x1p24f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t x = wb[h];
+      const uint32_t a = x & 0x00FF00FFu;                         // columns 4j, 4j+2
+      const uint32_t c = __builtin_amdgcn_perm(x, x, 0x0C030C01u);  // columns 4j+1, 4j+3
+      f[4 * h + 0] = fma_mix<false>(a, m24, mb);
+      f[4 * h + 2] = fma_mix<true>(a, m24, mb);
+      f[4 * h + 1] = fma_mix<false>(c, m24, mb);
+      f[4 * h + 3] = fma_mix<true>(c, m24, mb);
+    }
+  }
+}
+
+// All 32 elements of a lane.  With two groups per lane (GPL = 2, 16-element
+// groups) elements 0-15 take m[0] and elements 16-31 m[1].
 template <int BITS, int GPL>
 __device__ __forceinline__ void dequant_mix(const uint32_t (&xo)[Fmt<BITS>::NW], const float (&mm)[GPL],
                                             const float (&mbb)[GPL], float (&f)[EPL]) {
-  constexpr int NW = Fmt<BITS>::NW;
-  if constexpr (BITS == 4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float m = mm[GPL == 2 ? (2 * j) / NW : 0], mb = mbb[GPL == 2 ? (2 * j) / NW : 0];
-      const float m24 = m * 0x1p24f, m20 = m * 0x1p20f;
-      const uint32_t x = xo[j];
-      const uint32_t a = x & 0x000F000Fu;          // columns 8j, 8j+4
-      const uint32_t b = x & 0x00F000F0u;          // columns 8j+1, 8j+5 (times 16)
-      const uint32_t c = (x >> 8) & 0x000F000Fu;   // columns 8j+2, 8j+6
-      const uint32_t d = (x >> 8) & 0x00F000F0u;   // columns 8j+3, 8j+7 (times 16)
-      f[8 * j + 0] = fma_mix<false>(a, m24, mb);
-      f[8 * j + 4] = fma_mix<true>(a, m24, mb);
-      f[8 * j + 1] = fma_mix<false>(b, m20, mb);
-      f[8 * j + 5] = fma_mix<true>(b, m20, mb);
-      f[8 * j + 2] = fma_mix<false>(c, m24, mb);
-      f[8 * j + 6] = fma_mix<true>(c, m24, mb);
-      f[8 * j + 3] = fma_mix<false>(d, m20, mb);
-      f[8 * j + 7] = fma_mix<true>(d, m20, mb);
-    }
-  } else {
+  for (int b = 0; b < EPL / 8; ++b) {
+    float t[8];
+    dequant_mix_block<BITS>(&xo[b * (BITS == 4 ? 1 : 2)], mm[GPL == 2 ? b / 2 : 0],
+                            mbb[GPL == 2 ? b / 2 : 0], t);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float m24 = mm[GPL == 2 ? (2 * j) / NW : 0] * 0x1p24f, mb = mbb[GPL == 2 ? (2 * j) / NW : 0];
-      const uint32_t x = xo[j];
-      const uint32_t a = x & 0x00FF00FFu;                         // columns 4j, 4j+2
-      const uint32_t b = __builtin_amdgcn_perm(x, x, 0x0C030C01u);  // columns 4j+1, 4j+3
-      f[4 * j + 0] = fma_mix<false>(a, m24, mb);
-      f[4 * j + 2] = fma_mix<true>(a, m24, mb);
-      f[4 * j + 1] = fma_mix<false>(b, m24, mb);
-      f[4 * j + 3] = fma_mix<true>(b, m24, mb);
-    }
+    for (int i = 0; i < 8; ++i) f[8 * b + i] = t[i];
   }
 }
 
@@ -576,37 +596,61 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
     float* rp = &at_bytes(H.ref, (row * DK + L.col0) * 4u);
     if constexpr (POLICY == POL_YOKED) load_f32(R, rp);
 
-    // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha))
-    uint32_t xo[NW];
-    if constexpr (BDR) {
-      uint32_t kx[NW], k1[NW];
-      mask(1, 0, kx);
-      mask(2, 0, k1);
+    // Linear write under a frozen scale: w, the scale and the reciprocal are
+    // known before any element, so each block of eight is dequantised,
+    // written, read out and rounded in one pass and neither S' nor S is held
+    // for the whole row (fewer registers, more waves per SIMD).
+    constexpr bool ONE_PASS = !DELTA && POLICY == POL_PERSISTENT;
+    // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha));
+    // offset codes of words j0 .. j0+N-1, negated where k_c < 0 (BDR)
+    auto orient = [&](int j0, auto& d) {
+      constexpr int N = sizeof(d) / sizeof(d[0]);
+      if constexpr (BDR) {
+        uint32_t kx[N], k1[N];
+        mask(1, j0, kx);
+        mask(2, j0, k1);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) xo[j] = (in.x[j] ^ kx[j]) + k1[j];   // negated where k_c < 0
-    } else {
+        for (int j = 0; j < N; ++j) d[j] = (in.x[j0 + j] ^ kx[j]) + k1[j];
+      } else {
 #pragma unroll
-      for (int j = 0; j < NW; ++j) xo[j] = in.x[j] ^ F::OFF;
+        for (int j = 0; j < N; ++j) d[j] = in.x[j0 + j] ^ F::OFF;
+      }
+    };
+    uint32_t xo[ONE_PASS ? 1 : NW];
+    if constexpr (!ONE_PASS) orient(0, xo);
+    float m[GPL], mb[GPL];
+#pragma unroll
+    for (int h = 0; h < GPL; ++h) {
+      m[h] = in.s[h] * L.alpha_s;
+      mb[h] = -F::BIAS * m[h];
     }
-    float sp[EPL];
-    if constexpr (DIAG) {
-      unpack_offsets<BITS>(xo, sp);
-#pragma unroll
-      for (int b = 0; b < EPL / 8; ++b) {
+    // S' of the block of eight elements 8b .. 8b+7
+    auto dequant_block = [&](int b, float (&f)[8]) {
+      uint32_t wl[WPB];
+      const uint32_t* wb = &xo[ONE_PASS ? 0 : WPB * b];
+      if constexpr (ONE_PASS) {
+        orient(WPB * b, wl);
+        wb = wl;
+      }
+      if constexpr (DIAG) {
+        unpack_block<BITS>(wb, f);
         float ab[8];
         lds_block<DK>(ab, vec, aOff + 8 * b);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          sp[8 * b + i] = (sp[8 * b + i] - F::BIAS) * (in.s[GPL == 2 ? b / 2 : 0] * ab[i]);
+        for (int i = 0; i < 8; ++i) f[i] = (f[i] - F::BIAS) * (in.s[GPL == 2 ? b / 2 : 0] * ab[i]);
+      } else {
+        dequant_mix_block<BITS>(wb, m[GPL == 2 ? b / 2 : 0], mb[GPL == 2 ? b / 2 : 0], f);
       }
-    } else {
-      float m[GPL], mb[GPL];
+    };
+    float sp[ONE_PASS ? 1 : EPL];
+    if constexpr (!ONE_PASS) {
 #pragma unroll
-      for (int h = 0; h < GPL; ++h) {
-        m[h] = in.s[h] * L.alpha_s;
-        mb[h] = -F::BIAS * m[h];
+      for (int b = 0; b < EPL / 8; ++b) {
+        float t[8];
+        dequant_block(b, t);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sp[8 * b + i] = t[i];
       }
-      dequant_mix<BITS, GPL>(xo, m, mb, sp);
     }
 
     // delta correction u = S' . k and the write coefficient w = beta (v - u)
@@ -695,7 +739,42 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
 #pragma unroll
     for (int h = 0; h < GPL; ++h) snew[h] = in.s[h];
     float po = 0.f;
-    {
+    if constexpr (ONE_PASS) {
+      float inv[GPL];
+#pragma unroll
+      for (int h = 0; h < GPL; ++h) inv[h] = inv_scale(snew[h]);
+      bool in_range = false;
+      if constexpr (BDR) {
+        bool ok = true;
+#pragma unroll
+        for (int h = 0; h < GPL; ++h) {
+          const float mq = F::QMAX * fabsf(in.s[h] * L.alpha_hi);
+          ok = ok && fmaf(mq, inv[h], -F::QMAX) <= 0.f;
+        }
+        in_range = __all(ok);
+      }
+      auto pass = [&](auto in_range_t) {
+#pragma unroll
+        for (int b = 0; b < EPL / 8; ++b) {
+          float spb[8], stb[8], kb[8], qb[8];
+          dequant_block(b, spb);
+          lds_block<DK>(kb, vec, kOff + 8 * b);
+          lds_block<DK>(qb, vec, qOff + 8 * b);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            stb[i] = fmaf(w, kb[i], spb[i]);
+            po = fmaf(stb[i], qb[i], po);
+          }
+          round_block(in_range_t, stb, spb, inv[GPL == 2 ? b / 2 : 0], b);
+        }
+      };
+      if (in_range)
+        pass(std::true_type{});
+      else
+        pass(std::false_type{});
+      const float o = row_sum<LPR>(po);
+      if (live && L.lc == 0) at_bytes(H.o, row * 4u) = o;
+    } else {
       // rank-one write and readout o_r = S_t . q (before requantisation)
       float st[EPL];
 #pragma unroll
