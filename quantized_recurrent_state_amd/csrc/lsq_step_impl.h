@@ -133,13 +133,6 @@ __device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
   return r;
 }
 
-// max of two rounded values by their bit patterns (as signed integers): the
-// same order as the floats whenever one of them is >= 0, which always holds
-// here; no NaN canonicalisation of the inputs is needed.
-__device__ __forceinline__ float max_bits(float a, float b) {
-  return __int_as_float(max(__float_as_int(a), __float_as_int(b)));
-}
-
 // d[i] = a[i] * b + c rounded toward +infinity (i = 0..7).  The single-
 // precision rounding field of the MODE register is switched for exactly these
 // eight instructions and restored to round-to-nearest-even.
@@ -490,23 +483,26 @@ __device__ __forceinline__ float inv_scale(float s) {
 // which keeps them out of the register file: more waves fit on a SIMD.
 constexpr int kVecs = 5;   // k, q, alpha, natural k, natural q
 // Orientation masks of INT8 codes (three times eight words per lane) live in
-// LDS too; INT4's twelve words stay in registers.
-#ifndef LSQ_MASK_LDS_MIN_BITS
-#define LSQ_MASK_LDS_MIN_BITS 8
-#endif
-template <int BITS, int DK, int ROUND>
+// LDS when a row takes two passes (the delta rule, or a scale computed from
+// the updated row), which hold S' or S for the whole row; the one-pass linear
+// write under a frozen scale has registers to spare and keeps them in
+// registers (fewer LDS reads per row: the directional rounding of the INT8
+// Mamba-2-style workload runs within 5% of round-to-nearest that way, against
+// 20% with the masks in LDS).  INT4's twelve words always stay in registers.
+template <int BITS, int DK, int ROUND, int DELTA, int POLICY>
 struct LdsPlan {
   static constexpr int NW = Fmt<BITS>::NW;
   static constexpr int LPR = DK / EPL;
-  static constexpr bool MASKS = ROUND == RND_BDR && BITS >= LSQ_MASK_LDS_MIN_BITS;
+  static constexpr bool ONE_PASS = !DELTA && POLICY == POL_PERSISTENT;
+  static constexpr bool MASKS = ROUND == RND_BDR && BITS == 8 && !ONE_PASS;
   static constexpr int MASK_WORDS = MASKS ? 3 * NW * LPR : 0;   // Kf, Kx, K1 per column chunk
   static constexpr int WAVE_FLOATS = kVecs * DK + MASK_WORDS;
 };
-template <int BITS, int DK, int POLICY, int ROUND, int DIAG>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG>
 struct Lane {
   static constexpr bool BDR = ROUND == RND_BDR;
   static constexpr int NW = Fmt<BITS>::NW;
-  static constexpr bool REG_MASKS = BDR && !LdsPlan<BITS, DK, ROUND>::MASKS;
+  static constexpr bool REG_MASKS = BDR && !LdsPlan<BITS, DK, ROUND, DELTA, POLICY>::MASKS;
   int h, slice, lr, lc, col0, gl, gi;
   int vbase;          // float offset of this wave's vectors in the LDS array
   HeadPtrs H;         // this head's rows
@@ -538,14 +534,14 @@ __device__ __forceinline__ void lds_words(uint32_t (&d)[N], const float* lds, in
 // The row loop of one wave.  KZ: the head's key has a zero component (no
 // update direction there), so those elements drop their round-up candidate.
 template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF, bool KZ>
-__device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DIAG>& L,
+__device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DELTA, DIAG>& L,
                                          const float* vec) {
   // stored scale format, fixed per instance (SFMT_*): the other formats'
   // paths are compiled out
   constexpr int sfmt = SF;
   // vec + L.vbase + v*DK + L.col0: this lane's 32 columns of vector v
   const int base0 = L.vbase + L.col0;
-  using P = LdsPlan<BITS, DK, ROUND>;
+  using P = LdsPlan<BITS, DK, ROUND, DELTA, POLICY>;
   // vec + mbase0 + m*LPR*NW: this lane's words of mask m (Kf, Kx, K1)
   const int mbase0 = L.vbase + kVecs * DK + L.lc * P::NW;
   using F = Fmt<BITS>;
@@ -600,7 +596,7 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
     // known before any element, so each block of eight is dequantised,
     // written, read out and rounded in one pass and neither S' nor S is held
     // for the whole row (fewer registers, more waves per SIMD).
-    constexpr bool ONE_PASS = !DELTA && POLICY == POL_PERSISTENT;
+    constexpr bool ONE_PASS = P::ONE_PASS;
     // dequantise (oriented for BDR): S' = fma(u, m, -bias*m) = fl(C * fl(s*alpha));
     // offset codes of words j0 .. j0+N-1, negated where k_c < 0 (BDR)
     auto orient = [&](int j0, auto& d) {
@@ -669,16 +665,20 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
     const float w = L.beta * (in.v - u);
 
     uint32_t X[NW];
-    // orientation by sign(w) (directional rounding): folded into the sign of
-    // inv so that every update points up; w = 0 has no direction
-    const uint32_t wsign = fbits(w) & 0x80000000u;
-    const float mu = (w == 0.f) ? 0.f : F::MQ;
-    const uint32_t Wm = static_cast<uint32_t>(static_cast<int32_t>(fbits(w)) >> 31);
-    const uint32_t W1 = Wm & F::ONES;
-    // back from the oriented frame: negate offset codes by sign(w), then by sign(k_c)
+    // Orientation by sign(w) (directional rounding), for w < 0: the rounding
+    // runs on -S and -S' (inv and the rounding constant negated), so a rounded
+    // value is -(MQ + c) with c the code in the key-oriented frame; its low
+    // mantissa bits, which the packing takes, are those of MQ + c, and the
+    // clamp bounds are negated with it.  w = 0 (of either sign) has no
+    // direction and is not negated.
+    const uint32_t wsign = (BDR && w < 0.f) ? 0x80000000u : 0u;
+    const float mq_w = __uint_as_float(fbits(F::MQ) ^ wsign);          // +-MQ
+    const float top_w = mq_w + F::QMAX, bot_w = mq_w - F::QMAX;         // the clamp, negated with it
+    const float mu = (w == 0.f) ? 0.f : mq_w;
+    // back from the key-oriented frame: negate offset codes where k_c < 0
     auto unorient = [&](uint32_t x, uint32_t kf, uint32_t k1) -> uint32_t {
       if constexpr (BDR)
-        return ((((x ^ Wm) + W1) ^ kf) + k1) ^ F::OFF;
+        return ((x ^ kf) + k1) ^ F::OFF;
       else
         return x ^ F::OFF;
     };
@@ -700,15 +700,16 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
           float kb[8];
           lds_block<DK>(kb, vec, kOff + 8 * b);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) tu[i] = (kb[i] == 0.f) ? F::MQ - F::QMAX : tu[i];
+          for (int i = 0; i < 8; ++i) tu[i] = (kb[i] == 0.f) ? bot_w : tu[i];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float tz = fmaf(stb[i], inv_w, F::MQ);  // round half even of z, + MQ
+          const float tz = fmaf(stb[i], inv_w, mq_w);   // +-(MQ + round half even of z)
           if constexpr (IN_RANGE)
-            t[i] = __builtin_amdgcn_fmed3f(tz, tu[i], F::MQ + F::QMAX);
+            t[i] = __builtin_amdgcn_fmed3f(tz, tu[i], top_w);
           else
-            t[i] = __builtin_amdgcn_fmed3f(max_bits(tz, tu[i]), F::MQ - F::QMAX, F::MQ + F::QMAX);
+            t[i] = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(tz, tu[i], __builtin_inff()), bot_w,
+                                           top_w);   // max(tz, tu), then the clamp
         }
       } else if constexpr (ROUND == RND_DITHER) {
         // floor(z + u) with the Weyl offsets of elements 8b .. 8b+7
@@ -938,8 +939,8 @@ void step_kernel(StepArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wave >= a.total_waves) return;     // whole waves only
-  Lane<BITS, DK, POLICY, ROUND, DIAG> L;
-  using P = LdsPlan<BITS, DK, ROUND>;
+  Lane<BITS, DK, POLICY, ROUND, DELTA, DIAG> L;
+  using P = LdsPlan<BITS, DK, ROUND, DELTA, POLICY>;
   L.h = wave / a.waves_per_head;
   L.slice = wave - L.h * a.waves_per_head;
   {
