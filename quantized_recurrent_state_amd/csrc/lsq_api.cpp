@@ -190,6 +190,9 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
     a.head_scale = 1;
   }
   choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves);
+  // a state of 512 MiB or more does not stay in the 256 MB Infinity Cache
+  // between steps: its code loads take the non-temporal hint
+  a.nt_loads = (size_t)n_heads(c) * c.dv * c.dk * (size_t)c.bits / 8 >= ((size_t)512 << 20);
   constexpr uint32_t kWeyl = 0x9E3779B9u;   // 2^32 (sqrt(5)-1)/2, truncated
   a.dither_base = (uint32_t)((uint64_t)st->step * (uint64_t)c.dv * (uint64_t)c.dk) * kWeyl;
   a.dither_row = (uint32_t)c.dk * kWeyl;

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void bdr_alt_kernel(StepArgs a) {
     const uint32_t i = row_of(it);
 #pragma unroll
     for (int c = 0; c < NW / 4; ++c) {
-      const u32x4 w4 = load_codes16(codes_h + (i * ROWB + lc * LB + 16 * c));
+      const u32x4 w4 = load_codes16<>(codes_h + (i * ROWB + lc * LB + 16 * c));
       d.x[4 * c] = w4.x; d.x[4 * c + 1] = w4.y; d.x[4 * c + 2] = w4.z; d.x[4 * c + 3] = w4.w;
     }
     d.s = at_bytes(scales_h, (i * ng + gi) * 4u);

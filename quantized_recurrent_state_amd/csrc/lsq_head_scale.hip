@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void head_scale_kernel(StepArgs a) {
     uint32_t xo[NW];
 #pragma unroll
     for (int c = 0; c < NW / 4; ++c) {
-      const u32x4 w4 = load_codes16(cp + 16 * c);
+      const u32x4 w4 = load_codes16<>(cp + 16 * c);
       xo[4 * c + 0] = w4.x ^ F::OFF;
       xo[4 * c + 1] = w4.y ^ F::OFF;
       xo[4 * c + 2] = w4.z ^ F::OFF;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64 * NWV) void head_scale1_kernel(StepArgs a) {
   uint32_t xo[NW];
 #pragma unroll
   for (int c = 0; c < NW / 4; ++c) {
-    const u32x4 w4 = load_codes16(codes_h + (i * ROWB + lc * (EPL * BITS / 8) + 16 * c));
+    const u32x4 w4 = load_codes16<>(codes_h + (i * ROWB + lc * (EPL * BITS / 8) + 16 * c));
     xo[4 * c + 0] = w4.x ^ F::OFF;
     xo[4 * c + 1] = w4.y ^ F::OFF;
     xo[4 * c + 2] = w4.z ^ F::OFF;

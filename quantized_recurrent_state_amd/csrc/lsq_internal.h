@@ -40,6 +40,7 @@ struct StepArgs {
   int32_t lrb_cin, lrb_cout;  // b copy read / written this step
   int32_t sfmt;          // stored scale format: 0 fp32, 1 binary16, 2 bfloat16
   int32_t head_scale;    // 1: one scale per head (scales [n]), broadcast to every row
+  int32_t nt_loads;      // 1: the packed codes exceed the last-level cache by far (non-temporal loads)
 };
 
 // Arguments of a calibration launch: quantise an fp32 state into codes/scales.

@@ -349,25 +349,21 @@ __device__ __forceinline__ void pack_block(const float (&t)[8], uint32_t* X) {
 
 // 16-byte accesses of the packed codes.  Every state byte is written once per
 // step and not read again within it, so the stores carry the non-temporal
-// hint (the nt bit), which speeds up a read-then-write stream on gfx950 (3%
-// on the large steps).  Non-temporal loads gain about as much on states far
-// larger than the last-level cache but lose up to 15% on states that fit it
-// (their next step re-reads them from there), so the loads keep the default.
+// hint (the nt bit), which speeds up a read-then-write stream on gfx950.  The
+// loads carry it too (NTL) when the state is far larger than the last-level
+// cache: a head's span then streams as fast as a copy of it; on a state the
+// Infinity Cache holds between steps the hint would send the next step to
+// HBM, so those launches keep default loads.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#ifndef LSQ_NT_CODES
-#define LSQ_NT_CODES 2      // bit 0: loads, bit 1: stores
-#endif
+template <bool NTL = false>
 __device__ __forceinline__ u32x4 load_codes16(const uint8_t* p) {
-  if constexpr ((LSQ_NT_CODES & 1) != 0)
+  if constexpr (NTL)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   else
     return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void store_codes16(uint8_t* p, u32x4 v) {
-  if constexpr ((LSQ_NT_CODES & 2) != 0)
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else
-    *reinterpret_cast<u32x4*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 // Per-lane row data, loaded one iteration ahead.
@@ -418,14 +414,14 @@ __device__ __forceinline__ const T& at_bytes(const T* base, uint32_t byte_off) {
   return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
-template <int BITS, int DK, int GPL>
+template <int BITS, int DK, int GPL, bool NTL = false>
 __device__ __forceinline__ void load_row(RowIn<BITS, GPL>& R, const HeadPtrs& H, int ng, uint32_t r,
                                          int lc, int gi, int sfmt = SFMT_F32) {
   constexpr int ROWB = DK * BITS / 8;
   const uint8_t* p = H.codes + (r * ROWB + lc * (EPL * BITS / 8));
 #pragma unroll
   for (int c = 0; c < Fmt<BITS>::NW / 4; ++c) {
-    const u32x4 w = load_codes16(p + 16 * c);
+    const u32x4 w = load_codes16<NTL>(p + 16 * c);
     R.x[4 * c + 0] = w.x;
     R.x[4 * c + 1] = w.y;
     R.x[4 * c + 2] = w.z;
@@ -496,7 +492,13 @@ struct LdsPlan {
   static constexpr bool ONE_PASS = !DELTA && POLICY == POL_PERSISTENT;
   static constexpr bool MASKS = ROUND == RND_BDR && BITS == 8 && !ONE_PASS;
   static constexpr int MASK_WORDS = MASKS ? 3 * NW * LPR : 0;   // Kf, Kx, K1 per column chunk
-  static constexpr int WAVE_FLOATS = kVecs * DK + MASK_WORDS;
+  // Each vector is stored as LPR chunks of 32 floats, one per column chunk of
+  // a row, PAD floats apart: the chunks a wave's lanes read together (four at
+  // Dk = 128) then start in different LDS banks instead of all in bank 0.
+  static constexpr int PAD = 4;
+  static constexpr int CHUNK = EPL + PAD;
+  static constexpr int VSTRIDE = LPR * CHUNK;     // floats per staged vector
+  static constexpr int WAVE_FLOATS = kVecs * VSTRIDE + MASK_WORDS;
 };
 template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG>
 struct Lane {
@@ -533,17 +535,18 @@ __device__ __forceinline__ void lds_words(uint32_t (&d)[N], const float* lds, in
 
 // The row loop of one wave.  KZ: the head's key has a zero component (no
 // update direction there), so those elements drop their round-up candidate.
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF, bool KZ>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF, bool KZ,
+          bool NTL>
 __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DELTA, DIAG>& L,
                                          const float* vec) {
   // stored scale format, fixed per instance (SFMT_*): the other formats'
   // paths are compiled out
   constexpr int sfmt = SF;
-  // vec + L.vbase + v*DK + L.col0: this lane's 32 columns of vector v
-  const int base0 = L.vbase + L.col0;
   using P = LdsPlan<BITS, DK, ROUND, DELTA, POLICY>;
+  // vec + L.vbase + v*VSTRIDE + L.lc*CHUNK: this lane's 32 columns of vector v
+  const int base0 = L.vbase + L.lc * P::CHUNK;
   // vec + mbase0 + m*LPR*NW: this lane's words of mask m (Kf, Kx, K1)
-  const int mbase0 = L.vbase + kVecs * DK + L.lc * P::NW;
+  const int mbase0 = L.vbase + kVecs * P::VSTRIDE + L.lc * P::NW;
   using F = Fmt<BITS>;
   constexpr int NW = F::NW;
   constexpr int LPR = DK / EPL;          // lanes per row
@@ -585,8 +588,8 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       }
     };
     (void)mask;
-    const int kOff = base, qOff = base + DK, aOff = base + 2 * DK;
-    const int knOff = base + 3 * DK, qnOff = base + 4 * DK;
+    const int kOff = base, qOff = base + P::VSTRIDE, aOff = base + 2 * P::VSTRIDE;
+    const int knOff = base + 3 * P::VSTRIDE, qnOff = base + 4 * P::VSTRIDE;
     (void)qOff; (void)aOff; (void)knOff; (void)qnOff;
     float R[POLICY == POL_YOKED ? EPL : 4];
     float* rp = &at_bytes(H.ref, (row * DK + L.col0) * 4u);
@@ -909,25 +912,26 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
   RowIn<BITS, GPL> bufA, bufB;
   bool liveA, liveB;
   uint32_t rowA = row_of(0, liveA), rowB = 0;
-  load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
+  load_row<BITS, DK, GPL, NTL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
   for (int it = 0; it < a.nit; it += 2) {
     if (it + 1 < a.nit) {
       rowB = row_of(it + 1, liveB);
-      load_row<BITS, DK, GPL>(bufB, H, a.ng, rowB, L.lc, L.gi, sfmt);
+      load_row<BITS, DK, GPL, NTL>(bufB, H, a.ng, rowB, L.lc, L.gi, sfmt);
     }
     resolve_scales(bufA, sfmt);
     process(bufA, liveA, rowA);
     if (it + 1 >= a.nit) break;
     if (it + 2 < a.nit) {
       rowA = row_of(it + 2, liveA);
-      load_row<BITS, DK, GPL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
+      load_row<BITS, DK, GPL, NTL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
     }
     resolve_scales(bufB, sfmt);
     process(bufB, liveB, rowB);
   }
 }
 
-template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF>
+template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF,
+          bool NTL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSQ_STEP_WAVES_PER_EU)))
 void step_kernel(StepArgs a) {
   using F = Fmt<BITS>;
@@ -974,7 +978,7 @@ void step_kernel(StepArgs a) {
   if constexpr (DIAG) {
     float aa[EPL];
     load_f32(aa, a.alpha + (size_t)L.h * DK + L.col0);
-    if (writer) store_lds(vec + L.vbase + 2 * DK + L.col0, aa);
+    if (writer) store_lds(vec + L.vbase + 2 * P::VSTRIDE + L.lc * P::CHUNK, aa);
     float am = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(aa[e]));
@@ -1005,7 +1009,7 @@ void step_kernel(StepArgs a) {
       }
       if constexpr (P::MASKS) {
         if (writer) {
-          float* mp = vec + L.vbase + kVecs * DK + L.lc * NW;
+          float* mp = vec + L.vbase + kVecs * P::VSTRIDE + L.lc * NW;
           reinterpret_cast<uint32_t*>(mp)[j] = m;
           reinterpret_cast<uint32_t*>(mp + LPR * NW)[j] = m ^ F::OFF;
           reinterpret_cast<uint32_t*>(mp + 2 * LPR * NW)[j] = m & F::ONES;
@@ -1018,8 +1022,8 @@ void step_kernel(StepArgs a) {
     }
     if constexpr (POLICY == POL_YOKED) {
       if (writer) {
-        store_lds(vec + L.vbase + 3 * DK + L.col0, kk);
-        store_lds(vec + L.vbase + 4 * DK + L.col0, qq);
+        store_lds(vec + L.vbase + 3 * P::VSTRIDE + L.lc * P::CHUNK, kk);
+        store_lds(vec + L.vbase + 4 * P::VSTRIDE + L.lc * P::CHUNK, qq);
       }
     }
 #pragma unroll
@@ -1029,8 +1033,8 @@ void step_kernel(StepArgs a) {
     }
   }
   if (writer) {
-    store_lds(vec + L.vbase + 0 * DK + L.col0, kk);
-    store_lds(vec + L.vbase + 1 * DK + L.col0, qq);
+    store_lds(vec + L.vbase + 0 * P::VSTRIDE + L.lc * P::CHUNK, kk);
+    store_lds(vec + L.vbase + 1 * P::VSTRIDE + L.lc * P::CHUNK, qq);
   }
   // LDS accesses of one wave execute in order; the barrier keeps the compiler
   // from moving reads of the staged vectors above these writes.
@@ -1040,11 +1044,11 @@ void step_kernel(StepArgs a) {
 
   if constexpr (BDR) {
     if (__any(kzero))
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, true>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, true, NTL>(a, L, vec);
     else
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false, NTL>(a, L, vec);
   } else {
-    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false>(a, L, vec);
+    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false, NTL>(a, L, vec);
   }
 }
 
@@ -1056,13 +1060,22 @@ hipError_t launch_family(const StepArgs& a, int policy, int rounding, int delta,
   static_assert(SF == SFMT_F32 || SF == SFMT_F16 || SF == SFMT_BF16, "stored scale format");
   const dim3 grid((a.total_waves + 3) / 4), block(256);
   const int gpl = a.group < EPL ? 2 : 1;   // 16-element groups: two per lane
-#define LSQ_CASE(P, R, D, G)                                                               \
-  if (policy == P && rounding == R && delta == D && diag == G) {                           \
-    if (gpl == 2)                                                                          \
-      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 2, SF>), grid, block, 0, s, a); \
-    else                                                                                   \
-      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 1, SF>), grid, block, 0, s, a); \
-    return hipGetLastError();                                                              \
+  // non-temporal code loads for states far larger than the last-level cache,
+  // instantiated for the INT4 frozen-scale, scalar-decay, 32-or-more-element-
+  // group instances with fp32 scales and RNE or directional rounding (the long
+  // multi-layer decode: 2% faster there; the INT8 launch of the same stack
+  // measured slower with them)
+  constexpr bool NT_FAMILY = SF == SFMT_F32 && BITS == 4;
+#define LSQ_CASE(P, R, D, G)                                                                       \
+  if (policy == P && rounding == R && delta == D && diag == G) {                                   \
+    if (gpl == 2)                                                                                  \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 2, SF>), grid, block, 0, s, a);        \
+    else if (NT_FAMILY && P == POL_PERSISTENT && G == 0 && R != RND_DITHER && a.nt_loads)          \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 1, SF, NT_FAMILY && P == POL_PERSISTENT && G == 0 && R != RND_DITHER>), \
+                         grid, block, 0, s, a);                                                    \
+    else                                                                                           \
+      hipLaunchKernelGGL((step_kernel<BITS, DK, P, R, D, G, 1, SF>), grid, block, 0, s, a);        \
+    return hipGetLastError();                                                                      \
   }
 #define LSQ_CASES_PR(P, R) \
   LSQ_CASE(P, R, 0, 0) LSQ_CASE(P, R, 0, 1) LSQ_CASE(P, R, 1, 0) LSQ_CASE(P, R, 1, 1)
