@@ -152,12 +152,18 @@ def main() -> int:
     wall = time.perf_counter() - t0
 
     # ---- kernel time per launch: the next K steps one launch at a time, HIP events
-    # around every launch on the launch stream (outside the wall-clock region)
+    # around every launch on the launch stream (outside the wall-clock region).
+    # The arms' order alternates from step to step: where arms read the same
+    # inputs, the first launch of a step fetches them from HBM and the next finds
+    # them in the last-level cache, so each arm takes each position half the time.
     ev_s = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in arms]
     ev_e = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in arms]
     torch.cuda.synchronize()
     for j, t in enumerate(range(W + K, W + 2 * K)):
-        for i, a in enumerate(arms):
+        order = list(enumerate(arms))
+        if j % 2:
+            order.reverse()
+        for i, a in order:
             ev_s[i][j].record(stream)
             launch(a, t)
             ev_e[i][j].record(stream)
@@ -574,8 +580,8 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
     for a in arms:
         n = a["cfg"].n
         bph = runner.algorithmic_bytes(a["cfg"]) // n          # bytes per head-step
-        # the rate of one step on `threads` heads sets the sample size
-        ocfg, st, sel = sample(a, min(n, threads))
+        # the rate of one step on eight heads per thread sets the sample size
+        ocfg, st, sel = sample(a, min(n, 8 * threads))
         dt0 = max(timed(a, ocfg, st, sel, 1, threads), 1e-4)
         per_hs = dt0 / ocfg.n * threads                        # seconds per head-step, one thread
         budget = per_arm * threads / per_hs                    # head-steps that fit the budget
@@ -591,6 +597,7 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
         o1, s1, sel1 = sample(a, m1)
         dt1 = timed(a, o1, s1, sel1, steps, 1)
         results.append({"arm": a["arm"].name, "heads": m, "of_heads": n, "steps": steps,
+                        "seconds": round(dt, 2), "seconds_one_thread": round(dt1, 2),
                         "gbs": round(bph * m * steps / dt / 1e9, 4),
                         "head_steps_per_s": round(m * steps / dt, 1),
                         "gbs_one_thread": round(bph * m1 * steps / dt1 / 1e9, 4),
@@ -627,8 +634,9 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
             "head_steps_per_s": round(tot_hs / tot_dt, 1), "arms": results,
             "rounding_stats": rates,
             "sample": ("the whole workload as the GPU timed it" if whole else
-                       "evenly spaced heads of every arm x the steps that fit about "
-                       f"{per_arm:.0f} s per arm") +
+                       "evenly spaced heads of every arm x the steps sized to about "
+                       f"{per_arm:.0f} s per arm (" +
+                       ", ".join(f"{r['seconds']} s" for r in results) + " measured)") +
                       f"; from the GPU's state, on the same inputs; {threads} worker threads "
                       "(one per available core, at most 16), and one thread on 1/"
                       f"{threads} of the heads"}

@@ -536,9 +536,10 @@ __device__ __forceinline__ void lds_words(uint32_t (&d)[N], const float* lds, in
 // The row loop of one wave.  KZ: the head's key has a zero component (no
 // update direction there), so those elements drop their round-up candidate.
 template <int BITS, int DK, int POLICY, int ROUND, int DELTA, int DIAG, int GPL, int SF, bool KZ,
-          bool NTL>
+          bool NTL, bool PRE>
 __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLICY, ROUND, DELTA, DIAG>& L,
-                                         const float* vec) {
+                                         const float* vec, RowIn<BITS, GPL>& bufA, bool liveA,
+                                         uint32_t rowA) {
   // stored scale format, fixed per instance (SFMT_*): the other formats'
   // paths are compiled out
   constexpr int sfmt = SF;
@@ -909,10 +910,14 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
   };
 
   // Rows in pairs with two prefetch buffers (no register copies between rows).
-  RowIn<BITS, GPL> bufA, bufB;
-  bool liveA, liveB;
-  uint32_t rowA = row_of(0, liveA), rowB = 0;
-  load_row<BITS, DK, GPL, NTL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
+  // PRE: the caller has requested the first row (bufA, liveA, rowA) already
+  if constexpr (!PRE) {
+    rowA = row_of(0, liveA);
+    load_row<BITS, DK, GPL, NTL>(bufA, H, a.ng, rowA, L.lc, L.gi, sfmt);
+  }
+  RowIn<BITS, GPL> bufB;
+  bool liveB;
+  uint32_t rowB = 0;
   for (int it = 0; it < a.nit; it += 2) {
     if (it + 1 < a.nit) {
       rowB = row_of(it + 1, liveB);
@@ -971,6 +976,24 @@ void step_kernel(StepArgs a) {
   float kk[EPL], qq[EPL];
   load_f32(kk, a.k + (size_t)L.h * DK + L.col0);
   load_f32(qq, a.q + (size_t)L.h * DK + L.col0);
+  // The wave's first row (codes, scale, v) is requested before the head's
+  // vectors arrive, so that the two loads' latencies overlap, except in the
+  // persistent-BDR instances where holding that row through the set-up below
+  // would take the kernel past 128 VGPRs (below four waves per SIMD): INT8 with
+  // the delta rule or two groups per lane, INT4 with the delta rule and two
+  // groups per lane or a diagonal decay.  Those request it after the set-up.
+  constexpr bool HOIST = !(POLICY == POL_PERSISTENT && BDR &&
+                           (BITS == 8 ? (DELTA || GPL == 2) : (DELTA && (GPL == 2 || DIAG))));
+  RowIn<BITS, GPL> row0in;
+  bool live0 = false;
+  uint32_t row0 = 0;
+  if constexpr (HOIST) {
+    constexpr int RPI = 64 / LPR;
+    const int r = L.slice * a.nit * RPI + L.lr;
+    live0 = r < a.dv;
+    row0 = (uint32_t)min(r, a.dv - 1);
+    load_row<BITS, DK, GPL, NTL>(row0in, L.H, a.ng, row0, L.lc, L.gi, SF);
+  }
   L.alpha_s = DIAG ? 1.f : a.alpha[L.h];
   L.alpha_hi = fabsf(L.alpha_s);
   L.beta = a.beta[L.h];
@@ -1044,11 +1067,11 @@ void step_kernel(StepArgs a) {
 
   if constexpr (BDR) {
     if (__any(kzero))
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, true, NTL>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, true, NTL, HOIST>(a, L, vec, row0in, live0, row0);
     else
-      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false, NTL>(a, L, vec);
+      row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false, NTL, HOIST>(a, L, vec, row0in, live0, row0);
   } else {
-    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false, NTL>(a, L, vec);
+    row_loop<BITS, DK, POLICY, ROUND, DELTA, DIAG, GPL, SF, false, NTL, HOIST>(a, L, vec, row0in, live0, row0);
   }
 }
 
