@@ -6,7 +6,9 @@ oracle's reading: code = clamp(floor(S*inv + u)) with u the Weyl sequence
 frac(i * (sqrt(5)-1)/2) in 32-bit fixed point, i = step*Dv*Dk + r*Dk + c.
 These tests tie it to things other than its own formula:
   * the offsets it uses agree with frac(i * 0.6180339887...) computed here in
-    50-digit decimal arithmetic (up to the fixed-point error, which is bounded);
+    50-digit decimal arithmetic (up to the fixed-point error, which is bounded),
+    and exactly the top 23 bits of the 32-bit fixed-point rotation whose
+    constant is derived here from sqrt(5);
   * over many steps the codes average to the exact value (dither is unbiased,
     and a low-discrepancy sequence gets there at rate ~log(T)/T);
   * integers are left unchanged, out-of-range values clamp, every code is
@@ -61,6 +63,29 @@ def test_offsets_follow_the_golden_ratio_rotation():
                 assert codes[r, c] == (1 if u >= thr else 0), (t, r, c)
                 checked += 1
     assert checked > len(steps) * 4 * 64 - 40
+
+
+def test_offsets_are_the_fixed_point_rotation_on_a_23_bit_grid():
+    """The reading's exact form: the rotation in 32-bit fixed point (the
+    conjugate truncated to 32 fractional bits, derived here from sqrt(5), times
+    i modulo 1), of which the top 23 bits are kept so that 1 + u is an fp32
+    number in [1, 2).  Compared exactly, as rationals, at near and far
+    positions; the offsets the oracle used come from its trace."""
+    from fractions import Fraction
+    from decimal import ROUND_FLOOR
+    phi32 = int((PHI_C * 2 ** 32).to_integral_value(rounding=ROUND_FLOOR))
+    for t in (0, 1, 3, 77, 50_000):
+        cfg = _cfg(step=t)
+        tr = {}
+        _step_constant(cfg, [0.5, 0.25, 0.75, 0.125], trace=tr)
+        u = tr["yp"][0]
+        for r in range(cfg.dv):
+            for c in range(cfg.dk):
+                i = t * cfg.dv * cfg.dk + r * cfg.dk + c
+                frac = Fraction((i * phi32) % 2 ** 32, 2 ** 32)
+                want = Fraction((frac * 2 ** 23).__floor__(), 2 ** 23)
+                assert Fraction(float(u[r, c])) == want, (t, r, c)
+                assert np.float32(1.0 + u[r, c]) == 1.0 + u[r, c]     # 1 + u is an fp32 number
 
 
 def test_dither_is_unbiased_over_steps():
