@@ -323,7 +323,9 @@ def measure_ceiling(dev, stream, gib: float, span_kib: int) -> dict:
     buffer, 16-byte vectors, 1-4 per lane, with and without the non-temporal
     hint), and the in-place span walk of the decode step's own access pattern
     (one wave per span of span_kib KiB).  Best of five launches each, HIP events
-    on the launch stream; GB/s counts bytes read plus bytes written."""
+    on the launch stream; GB/s counts bytes read plus bytes written.  Also the
+    VALU issue rate of fma, med3 and a four-and-four mix at four waves per SIMD
+    (lsq_probe_valu), in wave64 instructions per second."""
     import torch
     import quantized_recurrent_state_amd as lsq
 
@@ -363,6 +365,25 @@ def measure_ceiling(dev, stream, gib: float, span_kib: int) -> dict:
             best = {"gbs": g, "span_kib": span_kib, "nontemporal_loads": nt}
     out["span_in_place"] = best
     del src, dst
+    # VALU issue rates of one instruction form at four waves per SIMD (the
+    # reference for an arithmetic-bound kernel): wave64 instructions per second
+    sink = torch.zeros(4, device=dev)
+    wg, iters = 1024, 8192
+    for name, form in (("fma", lsq.PROBE_VALU_FMA), ("med3", lsq.PROBE_VALU_MED3),
+                       ("mixed", lsq.PROBE_VALU_MIXED)):
+        run = lambda: lsq.lsq_probe_valu(form, wg, iters, sink, stream)
+        run()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(5)]
+        for a, b in ev:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = min(a.elapsed_time(b) for a, b in ev)
+        rate = wg * 4 * iters * 8 / (ms * 1e-3)
+        out.setdefault("valu", {})[name] = {"wave_instr_per_s": round(rate / 1e9, 2) * 1e9,
+                                            "per_cu_per_ns": round(rate / 256 / 1e9, 3)}
     log(f"ceiling probes: {out}")
     return out
 

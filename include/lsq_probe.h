@@ -3,7 +3,8 @@
  *
  * Not part of the decode step: a plain read, write or copy stream over one
  * device buffer, timed by the caller, that measures the rate a hand-written
- * kernel reaches on this part.  It is the practical ceiling against which the
+ * kernel reaches on this part (and, lsq_probe_valu below, the VALU issue rate
+ * of one instruction form).  It is the practical ceiling against which the
  * decode step's bandwidth is judged: the step reads and rewrites its packed
  * state every token ("Preserving Updates in Low-Bit Recurrent State
  * Quantization", abstract: high-precision states cost memory and bandwidth at
@@ -60,6 +61,29 @@ lsq_status lsq_probe_stream(int32_t kind, const void* src, void* dst, size_t byt
  * a launch failure. */
 lsq_status lsq_probe_span(const void* src, void* dst, size_t bytes, int32_t span_kib,
                           int32_t nontemporal, void* stream);
+
+typedef enum {
+  LSQ_PROBE_VALU_FMA = 0,    /* v_fma_f32, every operand a VGPR (the fast issue class) */
+  LSQ_PROBE_VALU_MED3 = 1,   /* v_med3_f32 (the slow issue class) */
+  LSQ_PROBE_VALU_MIXED = 2   /* four of each per iteration */
+} lsq_probe_valu_form;
+
+/* VALU issue probe: the rate at which this part retires one instruction form
+ * when nothing else limits it, the reference for a kernel whose arithmetic,
+ * not its memory traffic, sets its time (the packed-state decode step under
+ * directional rounding is one).  `workgroups` workgroups of 256 lanes (4
+ * waves); every lane runs `iters` iterations of eight independent chains of
+ * the form, so one launch issues workgroups * 4 * iters * 8 wave64
+ * instructions of it (1024 workgroups fill the chip's SIMDs four waves deep).
+ * No memory is read; out (4 bytes) is written only if the chains' sum equals
+ * a value they cannot produce, which keeps the compiler from removing them.
+ *   form        lsq_probe_valu_form
+ *   workgroups  >= 1
+ *   iters       >= 1
+ * INVALID_ARG for a bad form or count or a null out; HIP for a launch
+ * failure. */
+lsq_status lsq_probe_valu(int32_t form, int32_t workgroups, int32_t iters, float* out,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,8 @@ __all__ = ["LsqConfig", "LsqState", "LsqError", "lsq_state_sizes", "lsq_state_al
            "lsq_state_free", "lsq_state_zero", "lsq_state_calibrate", "lsq_state_dequantize", "lsq_state_set_calibrated",
            "lsq_state_step_index", "lsq_state_set_step_index",
            "lsq_decode_step", "lsq_decode_run", "lsq_prefill", "lsq_status_string", "lsq_version",
-           "lsq_probe_stream", "lsq_probe_span"]
+           "lsq_probe_stream", "lsq_probe_span",
+           "lsq_probe_valu"]
 
 
 @dataclass(frozen=True)
@@ -159,6 +160,16 @@ def lsq_probe_span(src, dst, nbytes: int, span_kib: int = 10, nontemporal: int =
     """Every wave walks its own span of src, rewriting it to dst (include/lsq_probe.h)."""
     _lib.check(_lib.load().lsq_probe_span(_ptr(src), _ptr(dst), nbytes, span_kib, nontemporal,
                                           _stream_ptr(stream)), "lsq_probe_span")
+
+
+PROBE_VALU_FMA, PROBE_VALU_MED3, PROBE_VALU_MIXED = 0, 1, 2
+
+
+def lsq_probe_valu(form: int, workgroups: int, iters: int, out, stream=None) -> None:
+    """VALU issue probe (include/lsq_probe.h): workgroups * 4 * iters * 8 wave64
+    instructions of one form; out is a device tensor of at least 4 bytes."""
+    _lib.check(_lib.load().lsq_probe_valu(form, workgroups, iters, _ptr(out), _stream_ptr(stream)),
+               "lsq_probe_valu")
 
 
 class LsqState:

@@ -74,6 +74,7 @@ def load() -> ctypes.CDLL:
         "lsq_probe_stream": [ctypes.c_int32, P, P, S, ctypes.c_int32, ctypes.c_int32,
                              ctypes.c_int32, P],
         "lsq_probe_span": [P, P, S, ctypes.c_int32, ctypes.c_int32, P],
+        "lsq_probe_valu": [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)

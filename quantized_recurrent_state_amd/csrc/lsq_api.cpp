@@ -520,6 +520,18 @@ lsq_status lsq_probe_span(const void* src, void* dst, size_t bytes, int32_t span
   return ok();
 }
 
+lsq_status lsq_probe_valu(int32_t form, int32_t workgroups, int32_t iters, float* out,
+                          void* stream) {
+  if (form != LSQ_PROBE_VALU_FMA && form != LSQ_PROBE_VALU_MED3 && form != LSQ_PROBE_VALU_MIXED)
+    return fail(LSQ_ERR_INVALID_ARG, "VALU probe form must be FMA, MED3 or MIXED");
+  if (workgroups < 1 || iters < 1)
+    return fail(LSQ_ERR_INVALID_ARG, "VALU probe needs at least one workgroup and one iteration");
+  if (!out) return fail(LSQ_ERR_INVALID_ARG, "VALU probe output must be non-null");
+  hipError_t e = lsq::launch_probe_valu(form, workgroups, iters, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "probe launch");
+  return ok();
+}
+
 const char* lsq_status_string(lsq_status s) {
   switch (s) {
     case LSQ_OK: return "LSQ_OK";

@@ -118,5 +118,7 @@ hipError_t launch_probe(int kind, const void* src, void* dst, size_t bytes, int 
                         int nontemporal, int workgroups, hipStream_t s);
 hipError_t launch_probe_span(const void* src, void* dst, size_t bytes, int span_kib, int nontemporal,
                              hipStream_t s);
+// VALU issue probe (include/lsq_probe.h): form 0 fma, 1 med3, 2 mixed.
+hipError_t launch_probe_valu(int form, int workgroups, int iters, float* out, hipStream_t s);
 
 }  // namespace lsq

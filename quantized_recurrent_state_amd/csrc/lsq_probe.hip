@@ -107,7 +107,43 @@ hipError_t launch_u(const void* src, void* dst, size_t n16, int u, int wg, hipSt
   return hipGetLastError();
 }
 
+// VALU issue probe: eight independent chains per lane of one instruction
+// form (0 fma, 1 med3, 2 four of each).  The operands are forced into VGPRs:
+// with a kernel argument (an SGPR) as an operand, an fma issues at the slow
+// rate.
+template <int FORM>
+__global__ __launch_bounds__(256) void valu_kernel(float* out, float x, float y, int iters) {
+  float xv = x, yv = y;
+  asm volatile("" : "+v"(xv), "+v"(yv));
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (float)(threadIdx.x + j);
+#pragma unroll 4
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (FORM == 0 || (FORM == 2 && j < 4))
+        a[j] = fmaf(a[j], xv, yv);
+      else
+        a[j] = __builtin_amdgcn_fmed3f(a[j], xv, yv);
+    }
+  }
+  const float s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  if (s == -1234.5f) out[0] = s;
+}
+
 }  // namespace dev
+
+hipError_t launch_probe_valu(int form, int workgroups, int iters, float* out, hipStream_t s) {
+  const dim3 grid(workgroups), block(256);
+  // x, y keep the chains finite: fma contracts towards y / (1 - x); med3 stays in [x, y]
+  const float x = 0.999f, y = 0.5f;
+  if (form == 0) hipLaunchKernelGGL((dev::valu_kernel<0>), grid, block, 0, s, out, x, y, iters);
+  else if (form == 1) hipLaunchKernelGGL((dev::valu_kernel<1>), grid, block, 0, s, out, x, y, iters);
+  else if (form == 2) hipLaunchKernelGGL((dev::valu_kernel<2>), grid, block, 0, s, out, x, y, iters);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_span(const void* src, void* dst, size_t bytes, int span_kib, int nontemporal,
                              hipStream_t s) {

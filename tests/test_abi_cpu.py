@@ -234,6 +234,15 @@ def test_probe_argument_checks_before_launch():
     assert L.lsq_probe_stream(1, None, FAKE, 0, 1, 1, 7, None) == 0
 
 
+def test_probe_valu_argument_checks_before_launch():
+    L = _lib.load()
+    assert L.lsq_probe_valu(3, 1024, 8, FAKE, None) == 1      # form
+    assert L.lsq_probe_valu(-1, 1024, 8, FAKE, None) == 1
+    assert L.lsq_probe_valu(0, 0, 8, FAKE, None) == 1         # workgroups
+    assert L.lsq_probe_valu(1, 1024, 0, FAKE, None) == 1      # iterations
+    assert L.lsq_probe_valu(2, 1024, 8, None, None) == 1      # null out
+
+
 def test_probe_span_argument_checks_before_launch():
     L = _lib.load()
     assert L.lsq_probe_span(FAKE, FAKE, 10240, 3, 1, None) == 1        # span

@@ -57,3 +57,18 @@ def test_span_walk_rewrites_every_vector(span, nt):
     torch.cuda.synchronize()
     assert torch.equal(dst[: nbytes // 4].view(-1, 4), want)
     assert not dst[nbytes // 4:].any()
+
+
+@pytest.mark.parametrize("form", [lsq.PROBE_VALU_FMA, lsq.PROBE_VALU_MED3, lsq.PROBE_VALU_MIXED])
+def test_valu_probe_runs_and_writes_nothing(form):
+    """The chains stay finite and never hit the sentinel, so out is untouched;
+    a longer run takes longer (the work is not optimised away)."""
+    out = torch.full((4,), 7.0, device=DEV)
+    lsq.lsq_probe_valu(form, 1024, 64, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.full((4,), 7.0, device=DEV))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(); lsq.lsq_probe_valu(form, 1024, 256, out); ev[1].record()
+    ev[2].record(); lsq.lsq_probe_valu(form, 1024, 4096, out); ev[3].record()
+    torch.cuda.synchronize()
+    assert ev[2].elapsed_time(ev[3]) > 4 * ev[0].elapsed_time(ev[1])
