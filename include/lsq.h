@@ -15,9 +15,10 @@
  * decode step with uniform group-wise INT4/INT8, the group scale being
  *   DYNAMIC    read from the new state itself (per-token absmax; project page,
  *              mechanism paragraph),
- *   PERSISTENT frozen once by calibration ("plain persistent scaling"),
- *   YOKED      read from an fp32 reference state advanced alongside ("the same
- *              grid, the same bit-width, but the loop cut"),
+ *   PERSISTENT frozen once by calibration (the abstract's persistent arm),
+ *   YOKED      read from an fp32 reference state advanced alongside (the
+ *              project page's control arm: the same quantiser, with the scale
+ *              no longer fed back from the quantised state),
  * and rounded either to nearest-even or by Bounded Directional Rounding
  * ("Preserving Updates in Low-Bit Recurrent State Quantization", abstract): an
  * element whose rounded value moved opposite to its update is rounded one
@@ -77,9 +78,9 @@
  *          followed by b [heads][2][r][Dk] (copy 1 used by diagonal decay).
  *
  * Low-Rank Bypass ("Preserving Updates in Low-Bit Recurrent State
- * Quantization", abstract: small updates accumulate in a compact low-rank
- * buffer whose sufficiently large elements are merged into the state
- * periodically; rank, period and threshold are not given there).  This
+ * Quantization", abstract: small updates collect in a low-rank buffer, and
+ * the parts of it that have grown large enough enter the state from time to
+ * time; rank, period and threshold are not given there).  This
  * library's reading: slot j holds a_j [Dv], b_j [Dk], B = sum_j a_j b_j^T;
  * at step t, n = t mod r slots are filled (the handle's step index t).  The
  * buffer decays with the state (scalar decay: a_j = fl(alpha a_j); diagonal:
@@ -216,7 +217,7 @@ lsq_status lsq_state_zero(lsq_state* st, void* stream);
  * group s = fl(absmax/qmax), codes clamp(RNE(S * fl(1/s))); the yoked policy
  * also copies S into ref; bits 32 copies S into f32.  Freezes the scales of a
  * persistent-policy handle (marks it calibrated).  This is the calibration of
- * "plain persistent scaling" ("When Dynamic Scaling Fails", abstract). */
+ * the persistent-scale arm of "When Dynamic Scaling Fails" (abstract). */
 lsq_status lsq_state_calibrate(lsq_state* st, const float* S, void* stream);
 
 /* The dequantised state: S [heads][Dv][Dk] fp32 (device, caller-owned, 16-byte

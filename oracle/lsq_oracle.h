@@ -24,7 +24,8 @@
  *    is requantised at every decode step with uniform group-wise INT4; the
  *    per-token dynamic scale is read from the state being quantised; the
  *    persistent (static) scale; the scale yoked to a full-precision reference
- *    run alongside ("same grid, same bit-width, loop cut").
+ *    run alongside (the same quantiser; only the source of the scale
+ *    changes).
  *  - "Preserving Updates in Low-Bit Recurrent State Quantization" (abstract):
  *    Bounded Directional Rounding rounds an element whose rounded value moved
  *    opposite to its update one step toward that update.
@@ -38,8 +39,9 @@
  *    element's position in one sequence that runs through the head's state
  *    row by row, step after step (i taken mod 2^32).
  *  - "Preserving Updates in Low-Bit Recurrent State Quantization" (abstract):
- *    Low-Rank Bypass accumulates small updates in a compact low-rank buffer
- *    and periodically merges its sufficiently large elements into the state.
+ *    Low-Rank Bypass collects small updates in a low-rank buffer and, from
+ *    time to time, moves the parts of it that have grown large enough into
+ *    the state.
  *    Rank, period, threshold and precision are unstated; the reading
  *    implemented here (lsqo_step_lrb): an fp32 buffer of r rank-one slots
  *    (a_j in R^Dv, b_j in R^Dk), B = sum_j a_j b_j^T, decayed with the state
@@ -50,8 +52,8 @@
  *    in slot order, requantised under the handle's scale policy and rounding
  *    (directional rounding takes as the update's sign the sign of the buffer
  *    value U = sum_j a_j b_j, itself built by fmas in slot order from 0), and
- *    the buffer is emptied: elements whose code changes are the merged
- *    "sufficiently large" ones, the rest of the buffer is dropped.  Between
+ *    the buffer is emptied: the elements whose code changes are the ones
+ *    large enough to enter the state, the rest of the buffer is dropped.  Between
  *    merges the state is requantised from S' alone.
  *  - "LinQuant: Functional Invariances for Low-Precision Linear Recurrences"
  *    (summary page), Methodology, Low-Precision Chunkwise Realization: the

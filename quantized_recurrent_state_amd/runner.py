@@ -4,8 +4,8 @@ Step t of a workload uses the inputs drawn for step index t; a persistent
 workload first runs W unquantised (fp32) steps from S_0 = 0 (step indices
 0..W-1), freezes the group scales of S_W (lsq_state_calibrate) and then runs
 its quantised steps from index W.  This is the persistent-scale set-up of the
-workloads ("fixed from absmax of the fp32 state after a 64-step unquantized
-warmup"); every other workload starts quantised from S_0 = 0.
+workloads: scales frozen from the group absmax of the fp32 state after 64
+unquantised warmup steps; every other workload starts quantised from S_0 = 0.
 """
 from __future__ import annotations
 
