@@ -648,12 +648,36 @@ def cpu_baseline(arms, seconds: float, steps_avail: int):
         ne = ocfg.n * ocfg.dv * ocfg.dk * nst
         rates.append({"arm": a["arm"].name, "steps": nst, "bdr_fired_rate": round(fired / ne, 5),
                       "clamp_rate": round(clamped / ne, 5)})
+    # one teacher-forced parity step per arm, untimed and after everything else:
+    # the GPU takes one more step from its current state and the oracle repeats
+    # it from the same state and inputs on 64 evenly spaced heads; codes, stored
+    # scales and outputs are compared bit for bit (tests.parity.compare_step)
+    import torch
+    import quantized_recurrent_state_amd as lsq
+    from tests.parity import compare_step
+    parity = []
+    for a in arms:
+        ocfg, before, sel = sample(a, min(a["cfg"].n, 64))
+        i = a["inp"]
+        lsq.lsq_decode_step(a["st"].handle, i["q"][0], i["k"][0], i["v"][0], i["alpha"][0],
+                            i["beta"][0], a["o"], a["o_ref"], torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        after = snapshot(a["st"], heads=sel)
+        o_gpu = a["o"].index_select(0, sel).cpu().numpy()
+        o_ref_gpu = None if a["o_ref"] is None else a["o_ref"].index_select(0, sel).cpu().numpy()
+        x = tuple(i[k][0].index_select(0, sel).cpu().numpy() for k in ("q", "k", "v", "alpha", "beta"))
+        rep = compare_step(ocfg, before, x, after, o_gpu, o_ref_gpu)
+        parity.append({"arm": a["arm"].name, "heads": int(sel.numel()), "step": int(ocfg.step),
+                       "codes": rep.codes, "codes_exact": rep.exact, "codes_failed": rep.failed,
+                       "scales_differ": rep.scales_differ, "outputs": rep.outputs,
+                       "outputs_differ": rep.o_differ, "bit_exact": bool(rep.ok)})
+    log(f"parity sample: {parity}")
     whole = all(r["heads"] == r["of_heads"] and r["steps"] == steps_avail for r in results)
     return {"value": round(tot_b / tot_dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "host_cores": host_cores, "cores_available": avail, "kind": "oracle",
             "value_one_thread": round(tot_b1 / tot_dt1 / 1e9, 4),
             "head_steps_per_s": round(tot_hs / tot_dt, 1), "arms": results,
-            "rounding_stats": rates,
+            "rounding_stats": rates, "parity": parity,
             "sample": ("the whole workload as the GPU timed it" if whole else
                        "evenly spaced heads of every arm x the steps sized to about "
                        f"{per_arm:.0f} s per arm (" +
