@@ -220,6 +220,12 @@ def main() -> int:
         if (tr.get("source_sha") == sha and tr.get("workload") == wl.name
                 and tr.get("arm") == dom_a["arm"].name):
             traffic = int(tr["hbm_bytes_per_launch"])
+            # measured bytes of the other profiled segments, attached to their arms
+            for a in arms:
+                a["traffic"] = traffic if a is dom_a else None
+                for seg in (tr.get("int8_segment"),):
+                    if seg and seg.get("arm") == a["arm"].name:
+                        a["traffic"] = int(seg["hbm_bytes_per_launch"])
 
     # ---- copy probe for counter calibration (outside the timed region)
     if args.copy_probe_gib > 0:
@@ -293,7 +299,13 @@ def main() -> int:
                              "rounding": a["cfg"].rounding, "scale_fmt": a["cfg"].scale_fmt,
                              "lrb_rank": a["cfg"].lrb_rank, "heads": a["cfg"].n,
                              "bytes_per_step": a["bytes"], "launch_us": a["launch_us"],
-                             "kernel_gbs": a["kernel_gbs"]} for a in arms],
+                             "kernel_gbs": a["kernel_gbs"],
+                             "kernel_head_steps_per_s": round(
+                                 a["cfg"].n / (a["launch_us"]["mean"] * 1e-6), 1),
+                             "traffic_bytes_per_launch": a.get("traffic"),
+                             "traffic_over_algorithmic": (
+                                 round(a["traffic"] / a["bytes"], 4) if a.get("traffic") else None)}
+                            for a in arms],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
