@@ -169,7 +169,7 @@ typedef enum { LSQ_SCALE_F32 = 0, LSQ_SCALE_F16 = 1, LSQ_SCALE_BF16 = 2 } lsq_sc
  *          the upper half of the fp32 pattern), and the codes are formed with
  *          that stored value: inv = fl(1/s_stored); elements beyond qmax
  *          steps of a scale that rounded down clamp.  Quantised states only;
- *          not with the bypass or lsq_prefill.  INT4 g32 with bfloat16
+ *          not with the bypass.  INT4 g32 with bfloat16
  *          scales stores 4.5 bits per element (7.1x less than fp32), INT4
  *          g16 5 bits (6.4x).
  */
@@ -301,14 +301,17 @@ lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float*
  *              scale s = max|x| / 127 and round-half-even codes; the integer
  *              product is exact and H = fl(h * fl(s_V * s_K)),
  *   X          = fma(gamma^C, S, H), requantised in the state's own group
- *              format and policy with round-half-even; the dequantised state
- *              fl(code * s) is carried to the next chunk.
+ *              format and policy with round-half-even (a dynamic scale
+ *              rounded to the stored scale format first, as in the decode
+ *              step); the dequantised state fl(code * s) is carried to the
+ *              next chunk.
  * Inputs carry a leading [T] axis (contiguous, token-major): k [T][heads][Dk],
  * v [T][heads][Dv], alpha [T][heads] (or [T][heads][Dk] for a diagonal
  * decay), beta [T][heads]; device pointers, 4-byte aligned, read-only.
  * Supported: bits 4 and 8; policy DYNAMIC or PERSISTENT (calibrated first);
  * delta 0 (the delta-rule write is sequential per token: use
- * lsq_decode_run); no bypass (lrb_rank 0); Dk and Dv in {64, 128};
+ * lsq_decode_run); no bypass (lrb_rank 0); group scales along Dk (group >=
+ * Dk / 8, not one per head) in any stored format; Dk and Dv in {64, 128};
  * otherwise UNSUPPORTED.  The state pass rounds half to even whatever the
  * handle's rounding field says.  T = 0 or no heads: nothing to do.  The step
  * index advances by T.  One workgroup per head walks the chunks in order. */

@@ -442,7 +442,6 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
     return fail(LSQ_ERR_UNSUPPORTED, "prefill supports the DYNAMIC and PERSISTENT policies");
   if (c.delta != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill supports the linear write (delta 0)");
   if (c.lrb_rank != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill does not take the bypass");
-  if (c.scale_fmt != LSQ_SCALE_F32) return fail(LSQ_ERR_UNSUPPORTED, "prefill keeps fp32 scales");
   if (c.dv != 64 && c.dv != 128)
     return fail(LSQ_ERR_UNSUPPORTED, "dv %d: prefill has dv 64 and 128", c.dv);
   if (c.group == 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill needs group scales along Dk");
@@ -468,6 +467,7 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
   a.T = T;
   a.ng = c.dk / c.group;
   a.group = c.group;
+  a.sfmt = c.scale_fmt;
   hipError_t e = lsq::launch_prefill(a, c.bits, c.dk, c.dv, c.policy,
                                      c.decay == LSQ_DECAY_DIAG, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "prefill launch");

@@ -74,6 +74,7 @@ struct PrefillArgs {
   const float* alpha;    // [T][n] or [T][n][dk]
   const float* beta;     // [T][n]
   int32_t n_heads, T, ng, group;
+  int32_t sfmt;          // stored scale format (SFMT_*): fp32, binary16 or bfloat16
 };
 
 // Launch geometry shared by the host and the kernels.

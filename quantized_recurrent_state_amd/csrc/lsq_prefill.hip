@@ -7,8 +7,9 @@
 // fp32 suffix product of the chunk's later decays, gamma^C the chunk's
 // product; B V = fl(beta v); one INT8 absmax scale per operand block (head,
 // chunk); the integer product is exact, H = fl(h fl(s_V s_K)); X = fma(gamma,
-// S, H) requantised in the state's group format and policy (RNE); S carried as
-// fl(code s).
+// S, H) requantised in the state's group format and policy (RNE; a dynamic
+// scale is rounded to the stored scale format, fp32, binary16 or bfloat16,
+// before the codes are formed); S carried as fl(code s).
 //
 // One workgroup of eight waves per head walks the chunks in order, as a
 // three-stage pipeline with one barrier per chunk.  Waves 0-3 build operands,
@@ -56,7 +57,9 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-template <int BITS, int DK, int DV, int POLICY, int DIAG>
+// S16: the state's group scales are stored in a 16-bit format (a.sfmt picks
+// binary16 or bfloat16); the fp32 instances carry no conversion code.
+template <int BITS, int DK, int DV, int POLICY, int DIAG, bool S16>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
   constexpr int RT = DV / 64;            // 16-row tiles per state wave
@@ -98,7 +101,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<uint32_t*>(&stage[r * SP + 4 * w]) = word;
     }
   }
-  for (int idx = tid; idx < DV * ng; idx += 512) sscale[idx] = a.scales[hrow0 * ng + idx];
+  // scales as the fp32 values they represent (a 16-bit scale converts exactly)
+  const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(a.scales);
+  for (int idx = tid; idx < DV * ng; idx += 512)
+    sscale[idx] = S16 ? scale_from16(scales16[hrow0 * ng + idx], a.sfmt) : a.scales[hrow0 * ng + idx];
 
   const int64_t nh = a.n_heads;
   const bool krole = wave < KW, vrole = wave >= 2 && wave < 2 + VW;
@@ -272,6 +278,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
             m[I] = fmaxf(m[I], __shfl_xor(m[I], 16));
             m[I] = fmaxf(m[I], __shfl_xor(m[I], 32));
             s[I] = m[I] / QMAX;
+            // a 16-bit format: the stored value forms the codes
+            if constexpr (S16) s[I] = scale_from16(scale_to16(s[I], a.sfmt), a.sfmt);
             if (lane < 16 && (I % tpg) == 0) sscale[r * ng + (16 * I) / g] = s[I];
           }
         }
@@ -308,7 +316,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     ocodes[idx] = word;
   }
   if constexpr (POLICY == POL_DYNAMIC) {
-    for (int idx = tid; idx < DV * ng; idx += 512) a.scales[hrow0 * ng + idx] = sscale[idx];
+    uint16_t* out16 = reinterpret_cast<uint16_t*>(a.scales);
+    for (int idx = tid; idx < DV * ng; idx += 512) {
+      if constexpr (S16)   // already a value of the format: the conversion is exact
+        out16[hrow0 * ng + idx] = (uint16_t)scale_to16(sscale[idx], a.sfmt);
+      else
+        a.scales[hrow0 * ng + idx] = sscale[idx];
+    }
   }
 }
 
@@ -319,7 +333,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int bits, int dk, int dv, int po
   const dim3 grid(a.n_heads), block(512);
 #define LSQ_PF(B, DK, DV, P, G)                                                                   \
   if (bits == B && dk == DK && dv == DV && policy == P && diag == G) {                           \
-    hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G>), grid, block, 0, s, a);            \
+    if (a.sfmt == dev::SFMT_F32)                                                                 \
+      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, false>), grid, block, 0, s, a);   \
+    else                                                                                         \
+      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, true>), grid, block, 0, s, a);    \
     return hipGetLastError();                                                                    \
   }
 #define LSQ_PF_PG(B, DK, DV) \

@@ -7,6 +7,7 @@ own round-half-even requantisation), so the codes and scales are held bit for
 bit, free-running over every chunk of the prompt, not teacher-forced.
 Cases: INT4/INT8, Dk and Dv 64/128, dynamic and persistent scales, scalar and
 diagonal decay, prompts that end mid-chunk, single tokens, the group sizes,
+binary16 and bfloat16 scales,
 a prompt split over several calls, a decode step after a prefill, and the
 full-size workload (batch 64 x 16 heads, 4096 tokens) on sampled heads.
 """
@@ -99,6 +100,28 @@ def test_prefill_group_sizes(bits, group):
     st.prefill(dg["k"], dg["v"], dg["alpha"], dg["beta"])
     torch.cuda.synchronize()
     _check(cfg, st, before, dn, f"bits={bits} g={group}")
+
+
+@pytest.mark.parametrize("bits,pol,fmt,dc,group", [
+    (b, p, f, dc, 32 if b == 4 else 64)
+    for b in (4, 8)
+    for p in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+    for f in (lsq.SCALE_F16, lsq.SCALE_BF16)
+    for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)] + [
+    (4, lsq.POLICY_DYNAMIC, lsq.SCALE_BF16, lsq.DECAY_DIAG, 16),
+    (8, lsq.POLICY_DYNAMIC, lsq.SCALE_F16, lsq.DECAY_SCALAR, 128)])
+def test_prefill_16bit_scales(bits, pol, fmt, dc, group):
+    """binary16 and bfloat16 group scales: a dynamic scale is rounded to the
+    stored format at every chunk before the codes are formed, a persistent one
+    is read in the format; codes and stored scales bit for bit."""
+    cfg = lsq.LsqConfig(batch=1, heads=3, dk=128, dv=128, bits=bits, group=group, policy=pol,
+                        delta=0, decay=dc, scale_fmt=fmt)
+    st = _state(cfg)
+    before = snapshot(st)
+    dg, dn = _inputs(_recipe(dc), cfg.n, cfg.dk, cfg.dv, 150, seed=13)
+    st.prefill(dg["k"], dg["v"], dg["alpha"], dg["beta"])
+    torch.cuda.synchronize()
+    _check(cfg, st, before, dn, str(cfg))
 
 
 def test_prefill_from_zero_state_and_empty_prompt():

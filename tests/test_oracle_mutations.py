@@ -134,6 +134,9 @@ MUTANTS = {
         "GK[t * dk + c] = G[t * da + 0] * k[row * dk + c];")]),
     "prefill with one operand scale": ("prefill", [(
         "      const float sc = s_v * s_k;", "      const float sc = s_v * s_v;")]),
+    "prefill scale not rounded to the stored format": ("prefill", [(
+        "            snew = scale_as_stored(amax / (float)qm, cfg->scale_fmt);\n          }",
+        "            snew = amax / (float)qm;\n          }")]),
     "prefill with the chunk's first decay": ("prefill", [(
         "          const float* at = alpha + ((int64_t)(t0 + t) * nh + h) * da;",
         "          const float* at = alpha + ((int64_t)(t0) * nh + h) * da;")]),

@@ -16,6 +16,8 @@ S_[i+1] = Q(gamma^C S_[i] + H).  Tied here to things other than its own code:
     step vanish across chunks but add up inside one;
   * INT8 operand codes round half to even (exact ties exposed through the
     dynamic state scale);
+  * a binary16 stored scale forms the codes (numpy's rounding of the exact
+    group absmax over qmax);
   * T = 0 changes nothing.
 """
 import numpy as np
@@ -46,6 +48,31 @@ def test_grid_operands_give_the_exact_sum_within_half_a_step():
     assert np.all(np.abs(deq - X) <= 0.5 * s * (1 + 1e-6))
     Xg = np.abs(X).reshape(2, 32, 2, 32).max(-1)
     assert np.allclose(st.scales, Xg / 127, rtol=1e-6)
+
+
+def test_a_binary16_dynamic_scale_forms_the_codes():
+    """A stored binary16 scale (the scale-format reading): with grid operands one
+    chunk from a zero state makes X exact, so the stored scale must be numpy's
+    binary16 rounding of fl(max|X| / qmax) and every code the round-half-even
+    of X times the fp32 reciprocal of that stored value, clamped."""
+    rng = np.random.default_rng(2)
+    cfg = _cfg().replace(scale_fmt=oracle.SCALE_F16)
+    T = 40
+    v = rng.integers(-127, 128, (T, 2, 32)) * 2.0 ** -7
+    k = rng.integers(-127, 128, (T, 2, 64)) * 2.0 ** -10
+    v[0, :, 0] = 127 * 2.0 ** -7
+    k[0, :, 0] = 127 * 2.0 ** -10
+    st = oracle.zero_state(cfg)
+    oracle.prefill(cfg, st, k, v, np.ones((T, 2)), np.ones((T, 2)), chunk=64)
+    X = np.einsum("tni,tnj->nij", v, k)                         # exact, and fp32-representable
+    amax = np.abs(X).reshape(2, 32, 2, 32).max(-1).astype(np.float32)
+    s16 = (amax / np.float32(127)).astype(np.float16).astype(np.float32)
+    assert np.array_equal(st.scales, s16)
+    inv = np.where(s16 > 0, np.float32(1) / np.where(s16 > 0, s16, 1), 0).astype(np.float32)
+    want = np.clip(np.rint(X * np.repeat(inv, 32, axis=-1).astype(np.float64)), -127, 127)
+    assert np.array_equal(st.codes, want.astype(np.int8))
+    # and the stored value differs from the fp32 scale somewhere, so the pin bites
+    assert np.any(s16 != amax / np.float32(127))
 
 
 @pytest.mark.parametrize("decay", [0, 1])
