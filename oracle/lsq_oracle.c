@@ -634,11 +634,13 @@ static float quantise_block_i8(const float* x, int64_t n, int8_t* q) {
 
 int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes, float* scales,
                  const float* k, const float* v, const float* alpha, const float* beta) {
-  if (lsqo_check_config(cfg) || cfg->bits == 32 || cfg->delta != 0 || T < 0 || chunk < 1 ||
-      cfg->group == 0)
+  if (lsqo_check_config(cfg) || cfg->bits == 32 || cfg->delta != 0 || T < 0 || chunk < 1)
     return -1;
   if (cfg->policy != LSQO_POLICY_DYNAMIC && cfg->policy != LSQO_POLICY_PERSISTENT) return -1;
-  const int dk = cfg->dk, dv = cfg->dv, g = cfg->group, ng = dk / g, qm = qmax_of(cfg->bits);
+  /* group 0: one scale per head, over the whole Dv x Dk state */
+  const int head = cfg->group == 0;
+  const int dk = cfg->dk, dv = cfg->dv, g = head ? cfg->dk : cfg->group, ng = dk / g;
+  const int qm = qmax_of(cfg->bits);
   const int diag = cfg->decay == LSQO_DECAY_DIAG;
   const int64_t nh = (int64_t)cfg->batch * cfg->heads;
   const int da = diag ? dk : 1;                 /* decay values per token */
@@ -651,9 +653,10 @@ int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes
   int8_t* Kq = (int8_t*)malloc((size_t)chunk * dk);
   for (int64_t h = 0; h < nh; ++h) {
     int8_t* Ch = codes + h * (int64_t)dv * dk;
-    float* sh = scales + h * (int64_t)dv * ng;
+    float* sh = head ? scales + h : scales + h * (int64_t)dv * ng;
     for (int r = 0; r < dv; ++r)
-      for (int c = 0; c < dk; ++c) S[r * dk + c] = (float)Ch[r * dk + c] * sh[r * ng + c / g];
+      for (int c = 0; c < dk; ++c)
+        S[r * dk + c] = (float)Ch[r * dk + c] * sh[head ? 0 : r * ng + c / g];
     for (int32_t t0 = 0; t0 < T; t0 += chunk) {
       const int tc = (T - t0 < chunk) ? (int)(T - t0) : chunk;
       /* decay products: Gamma->_t = prod_{s>t} alpha_s within the chunk */
@@ -676,6 +679,32 @@ int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes
       const float s_v = quantise_block_i8(BV, (int64_t)tc * dv, Vq);
       const float s_k = quantise_block_i8(GK, (int64_t)tc * dk, Kq);
       const float sc = s_v * s_k;
+      if (head) {
+        /* one scale per head: every element of X first, then the head's
+         * absmax (dynamic), then the codes */
+        float amax = 0.0f;
+        for (int r = 0; r < dv; ++r) {
+          float* x = S + r * dk;
+          for (int c = 0; c < dk; ++c) {
+            int64_t hacc = 0;
+            for (int t = 0; t < tc; ++t) hacc += (int64_t)Vq[t * dv + r] * (int64_t)Kq[t * dk + c];
+            const float H = (float)hacc * sc;
+            x[c] = fmaf(gam[diag ? c : 0], x[c], H);
+            const float a = fabsf(x[c]);
+            if (a > amax) amax = a;
+          }
+        }
+        float snew = sh[0];
+        if (cfg->policy == LSQO_POLICY_DYNAMIC) snew = scale_as_stored(amax / (float)qm, cfg->scale_fmt);
+        const float inv = (snew == 0.0f) ? 0.0f : 1.0f / snew;
+        for (int64_t i = 0; i < (int64_t)dv * dk; ++i) {
+          const double q = clampd(round_half_even((double)S[i] * (double)inv), -qm, qm);
+          Ch[i] = (int8_t)q;
+          S[i] = (float)q * snew;
+        }
+        sh[0] = snew;
+        continue;
+      }
       /* state pass, row by row */
       for (int r = 0; r < dv; ++r) {
         float* x = S + r * dk;

@@ -66,8 +66,9 @@
  *    scale per operand block (per head and chunk): s = fl(absmax/127), codes
  *    clamp(RNE(x fl(1/s))); the integer product is exact, H = fl(h fl(s_V s_K));
  *    the state pass is X = fma(gamma, S_[i], H) requantised in the state's
- *    own group format and policy with round-to-nearest-even, and S_[i] is the
- *    dequantised state fl(C s).
+ *    own group format and policy with round-to-nearest-even (with one scale
+ *    per head, group 0, a dynamic scale is taken over all of the head's X),
+ *    and S_[i] is the dequantised state fl(C s).
  *
  * State layout used by the oracle (unpacked, host memory, heads = batch*heads):
  *   codes  int8  [heads][Dv][Dk]        signed codes in [-qmax, qmax]
@@ -100,8 +101,8 @@ typedef struct {
   int32_t batch, heads, dk, dv;
   int32_t bits;     /* 4, 8, or 32 (unquantised fp32 state) */
   int32_t group;    /* group size along Dk (ignored for bits == 32); 0: one scale
-                       per head (dynamic or persistent, RNE or BDR, no bypass,
-                       no prefill; scales then hold [heads] values) */
+                       per head (dynamic or persistent, RNE or BDR, no bypass;
+                       scales then hold [heads] values) */
   int32_t policy;   /* LSQO_POLICY_* */
   int32_t rounding; /* LSQO_ROUND_* */
   int32_t delta;    /* 0: linear write, 1: delta-rule correction */
@@ -162,7 +163,7 @@ int lsqo_step_lrb(const lsqo_config* cfg, int8_t* codes, float* scales, float* l
  * or persistent policy; bits 4 or 8): chunks of `chunk` tokens, the last one
  * possibly shorter.  Inputs k [T][heads][Dk], v [T][heads][Dv], alpha
  * [T][heads] or [T][heads][Dk], beta [T][heads]; codes and scales updated in
- * place (scales stay for the persistent policy). */
+ * place (scales stay for the persistent policy); group 0: one scale per head. */
 int lsqo_prefill(const lsqo_config* cfg, int32_t T, int32_t chunk, int8_t* codes, float* scales,
                  const float* k, const float* v, const float* alpha, const float* beta);
 

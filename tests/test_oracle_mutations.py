@@ -115,11 +115,18 @@ MUTANTS = {
     "prefill token's own decay in Gamma": ("prefill", [(
         GAMMA, "          const float* at = alpha + ((int64_t)(t0 + t) * nh + h) * da;\n"
                "          acc = acc * at[a];\n          G[t * da + a] = acc;")]),
-    "prefill without gamma^C": ("prefill", [(
-        "          x[c] = fmaf(gam[diag ? c : 0], x[c], H);", "          x[c] = x[c] + H;")]),
-    "prefill product transposed": ("prefill", [(
-        "hacc += (int64_t)Vq[t * dv + r] * (int64_t)Kq[t * dk + c];",
-        "hacc += (int64_t)Vq[t * dv + (c % dv)] * (int64_t)Kq[t * dk + (r % dk)];")]),
+    # (each prefill edit is planted in both state passes, the per-group one and
+    # the per-head one, told apart by the lines around it)
+    "prefill without gamma^C": ("prefill", [
+        ("          x[c] = fmaf(gam[diag ? c : 0], x[c], H);\n        }",
+         "          x[c] = x[c] + H;\n        }"),
+        ("            x[c] = fmaf(gam[diag ? c : 0], x[c], H);\n            const float a",
+         "            x[c] = x[c] + H;\n            const float a")]),
+    "prefill product transposed": ("prefill", [
+        ("          for (int t = 0; t < tc; ++t) hacc += (int64_t)Vq[t * dv + r] * (int64_t)Kq[t * dk + c];\n          const",
+         "          for (int t = 0; t < tc; ++t) hacc += (int64_t)Vq[t * dv + (c % dv)] * (int64_t)Kq[t * dk + (r % dk)];\n          const"),
+        ("            for (int t = 0; t < tc; ++t) hacc += (int64_t)Vq[t * dv + r] * (int64_t)Kq[t * dk + c];",
+         "            for (int t = 0; t < tc; ++t) hacc += (int64_t)Vq[t * dv + (c % dv)] * (int64_t)Kq[t * dk + (r % dk)];")]),
     "prefill carries the unquantised state": ("prefill", [(
         "            x[c] = (float)q * snew;   /* the dequantised state carried to the next chunk */",
         "            (void)0;")]),
@@ -137,6 +144,9 @@ MUTANTS = {
     "prefill scale not rounded to the stored format": ("prefill", [(
         "            snew = scale_as_stored(amax / (float)qm, cfg->scale_fmt);\n          }",
         "            snew = amax / (float)qm;\n          }")]),
+    "prefill head scale over the last row only": ("prefill", [(
+        "        for (int r = 0; r < dv; ++r) {\n          float* x = S + r * dk;",
+        "        for (int r = 0; r < dv; ++r) {\n          amax = 0.0f;\n          float* x = S + r * dk;")]),
     "prefill with the chunk's first decay": ("prefill", [(
         "          const float* at = alpha + ((int64_t)(t0 + t) * nh + h) * da;",
         "          const float* at = alpha + ((int64_t)(t0) * nh + h) * da;")]),

@@ -18,6 +18,8 @@ S_[i+1] = Q(gamma^C S_[i] + H).  Tied here to things other than its own code:
     dynamic state scale);
   * a binary16 stored scale forms the codes (numpy's rounding of the exact
     group absmax over qmax);
+  * one scale per head: the dynamic scale covers all of the head's X, and a
+    frozen head scale is the same quantiser as group scales sharing it;
   * T = 0 changes nothing.
 """
 import numpy as np
@@ -73,6 +75,52 @@ def test_a_binary16_dynamic_scale_forms_the_codes():
     assert np.array_equal(st.codes, want.astype(np.int8))
     # and the stored value differs from the fp32 scale somewhere, so the pin bites
     assert np.any(s16 != amax / np.float32(127))
+
+
+def test_a_dynamic_head_scale_covers_the_whole_head():
+    """One scale per head (group 0): with grid operands one chunk from a zero
+    state makes X exact, so the head's scale must be fl(max over all of its
+    X / qmax) and every code the round-half-even of X times its reciprocal."""
+    rng = np.random.default_rng(4)
+    cfg = _cfg(group=0)
+    T = 40
+    v = rng.integers(-127, 128, (T, 2, 32)) * 2.0 ** -7
+    k = rng.integers(-127, 128, (T, 2, 64)) * 2.0 ** -10
+    v[0, :, 0] = 127 * 2.0 ** -7
+    k[0, :, 0] = 127 * 2.0 ** -10
+    st = oracle.zero_state(cfg)
+    oracle.prefill(cfg, st, k, v, np.ones((T, 2)), np.ones((T, 2)), chunk=64)
+    X = np.einsum("tni,tnj->nij", v, k)
+    s = (np.abs(X).reshape(2, -1).max(-1).astype(np.float32) / np.float32(127)).astype(np.float32)
+    assert np.array_equal(st.scales.reshape(2), s)
+    inv = (np.float32(1) / s).astype(np.float64)
+    want = np.clip(np.rint(X * inv[:, None, None]), -127, 127)
+    assert np.array_equal(st.codes, want.astype(np.int8))
+
+
+@pytest.mark.parametrize("decay", [0, 1])
+def test_a_frozen_head_scale_equals_groups_sharing_it(decay):
+    """A persistent scale per head s is the same quantiser as group scales all
+    equal to s: the two prefills agree bit for bit over several chunks."""
+    rng = np.random.default_rng(5)
+    T = 150
+    k = rng.standard_normal((T, 2, 64)).astype(np.float32) / 8
+    v = rng.standard_normal((T, 2, 32)).astype(np.float32)
+    a = (rng.uniform(0.9, 1.0, (T, 2, 64)) if decay else rng.uniform(0.9, 1.0, (T, 2))).astype(np.float32)
+    b = rng.uniform(0.2, 1.0, (T, 2)).astype(np.float32)
+    C0 = rng.integers(-127, 128, (2, 32, 64)).astype(np.int8)
+    s_head = np.array([0.011, 0.027], np.float32)
+    ch = _cfg(group=0, policy=oracle.POLICY_PERSISTENT, decay=decay)
+    cg = _cfg(group=32, policy=oracle.POLICY_PERSISTENT, decay=decay)
+    sh, sg = oracle.zero_state(ch), oracle.zero_state(cg)
+    sh.codes[:] = C0
+    sg.codes[:] = C0
+    sh.scales[:] = s_head.reshape(sh.scales.shape)
+    sg.scales[:] = s_head[:, None, None]
+    oracle.prefill(ch, sh, k, v, a, b, chunk=64)
+    oracle.prefill(cg, sg, k, v, a, b, chunk=64)
+    assert np.array_equal(sh.codes, sg.codes)
+    assert np.any(sh.codes != C0)
 
 
 @pytest.mark.parametrize("decay", [0, 1])
