@@ -156,14 +156,14 @@ typedef enum { LSQ_SCALE_F32 = 0, LSQ_SCALE_F16 = 1, LSQ_SCALE_BF16 = 2 } lsq_sc
  *          state (scales [heads] fp32): DYNAMIC (the absmax over every
  *          element after the step's update, so all rows are updated before
  *          any is requantised) or PERSISTENT (calibrated over the head), RNE
- *          or BDR, fp32 scale, no bypass, no prefill, Dv <= 1024.  INT4 with 16-element
+ *          or BDR, fp32 scale, no bypass, Dv <= 1024.  INT4 with 16-element
  *          groups and fp32 scales stores 6 bits per element, 5.33x less
  *          than an fp32 state.
  *   delta  0: linear write, 1: delta-rule correction
  *   scale_fmt  stored format of the group scales (the pages fix none; 16-bit
  *          scales are the scale-format variant of "Preserving Updates in
- *          Low-Bit Recurrent State Quantization", whose "up to 5.3x" memory
- *          figure leaves the format open).  A computed scale (dynamic, yoked,
+ *          Low-Bit Recurrent State Quantization", whose memory saving of at
+ *          most 5.3x leaves the format open).  A computed scale (dynamic, yoked,
  *          calibration) is rounded to the format, to nearest with ties to
  *          even (binary16 with subnormals, overflow to infinity; bfloat16 on
  *          the upper half of the fp32 pattern), and the codes are formed with
@@ -311,8 +311,9 @@ lsq_status lsq_decode_run(lsq_state* st, int32_t H, const float* q, const float*
  * Supported: bits 4 and 8; policy DYNAMIC or PERSISTENT (calibrated first);
  * delta 0 (the delta-rule write is sequential per token: use
  * lsq_decode_run); no bypass (lrb_rank 0); group scales along Dk (group >=
- * Dk / 8, not one per head) in any stored format; Dk and Dv in {64, 128};
- * otherwise UNSUPPORTED.  The state pass rounds half to even whatever the
+ * Dk / 8) in any stored format, or one scale per head (group 0: a dynamic
+ * head scale is taken over all of the head's X at every chunk); Dk and Dv in
+ * {64, 128}; otherwise UNSUPPORTED.  The state pass rounds half to even whatever the
  * handle's rounding field says.  T = 0 or no heads: nothing to do.  The step
  * index advances by T.  One workgroup per head walks the chunks in order. */
 lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,

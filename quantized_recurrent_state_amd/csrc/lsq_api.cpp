@@ -444,8 +444,8 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
   if (c.lrb_rank != 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill does not take the bypass");
   if (c.dv != 64 && c.dv != 128)
     return fail(LSQ_ERR_UNSUPPORTED, "dv %d: prefill has dv 64 and 128", c.dv);
-  if (c.group == 0) return fail(LSQ_ERR_UNSUPPORTED, "prefill needs group scales along Dk");
-  if (c.dk / c.group > 8) return fail(LSQ_ERR_UNSUPPORTED, "prefill holds at most 8 groups per row");
+  if (c.group != 0 && c.dk / c.group > 8)
+    return fail(LSQ_ERR_UNSUPPORTED, "prefill holds at most 8 groups per row");
   if (c.policy == LSQ_POLICY_PERSISTENT && !st->calibrated)
     return fail(LSQ_ERR_NOT_CALIBRATED, "persistent scale used before lsq_state_calibrate");
   if (T == 0 || n_heads(c) == 0) {
@@ -465,7 +465,7 @@ lsq_status lsq_prefill(lsq_state* st, int32_t T, const float* k, const float* v,
   a.beta = beta;
   a.n_heads = (int32_t)n_heads(c);
   a.T = T;
-  a.ng = c.dk / c.group;
+  a.ng = c.group ? c.dk / c.group : 0;       // group 0: one scale per head
   a.group = c.group;
   a.sfmt = c.scale_fmt;
   hipError_t e = lsq::launch_prefill(a, c.bits, c.dk, c.dv, c.policy,

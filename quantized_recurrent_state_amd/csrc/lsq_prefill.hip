@@ -57,9 +57,13 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// S16: the state's group scales are stored in a 16-bit format (a.sfmt picks
+// S16: the state's scales are stored in a 16-bit format (a.sfmt picks
 // binary16 or bfloat16); the fp32 instances carry no conversion code.
-template <int BITS, int DK, int DV, int POLICY, int DIAG, bool S16>
+// HEAD: one scale per head (group 0).  A dynamic head scale needs the absmax
+// of the whole head's X before any code is formed: the four state waves post
+// their maxima to LDS and meet at one more barrier per chunk, which the
+// operand waves also take, so that both roles count the same barriers.
+template <int BITS, int DK, int DV, int POLICY, int DIAG, bool S16, bool HEAD>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
   constexpr int RT = DV / 64;            // 16-row tiles per state wave
@@ -80,6 +84,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) float gam[2][DK];            // gamma^C per column
   __shared__ float wmax[2][4];                          // per operand wave block absmax
   __shared__ float opscale[2][2];                       // s_V, s_K
+  __shared__ float hmax[4];                             // per state wave |X| max (HEAD)
+  constexpr bool XB = HEAD && POLICY == POL_DYNAMIC;    // the extra barrier per chunk
 
   // ---- the head's packed state -> LDS codes and scales.  The state stays
   // there as codes between chunks: the carried value is fl(code * scale).
@@ -103,8 +109,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   }
   // scales as the fp32 values they represent (a 16-bit scale converts exactly)
   const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(a.scales);
-  for (int idx = tid; idx < DV * ng; idx += 512)
-    sscale[idx] = S16 ? scale_from16(scales16[hrow0 * ng + idx], a.sfmt) : a.scales[hrow0 * ng + idx];
+  if constexpr (HEAD) {
+    if (tid == 0) sscale[0] = S16 ? scale_from16(scales16[h], a.sfmt) : a.scales[h];
+  } else {
+    for (int idx = tid; idx < DV * ng; idx += 512)
+      sscale[idx] = S16 ? scale_from16(scales16[hrow0 * ng + idx], a.sfmt) : a.scales[hrow0 * ng + idx];
+  }
 
   const int64_t nh = a.n_heads;
   const bool krole = wave < KW, vrole = wave >= 2 && wave < 2 + VW;
@@ -199,11 +209,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
         cmax = wave_max(cmax);
         if (lane == 0) wmax[p & 1][wave] = cmax;
       }
+      if constexpr (XB) __syncthreads();   // the state waves' head maximum
       __syncthreads();
     }
   } else {
     __syncthreads();                     // iterations -2 and -1: operands only
     __syncthreads();
+    if constexpr (XB) {
+      __syncthreads();
+      __syncthreads();
+    }
     const int sw = wave - 4;
     for (int i = 0; i < nchunk; ++i) {
       const int slot = i & 1;
@@ -231,6 +246,60 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
       }
       // ---- state pass: X = fma(gamma, S, H), requantised per group
       const float sc = s_v * s_k;
+      if constexpr (HEAD) {
+        // one scale per head: X of both row tiles first, then the head's
+        // absmax (dynamic), then the codes
+        float x[RT][CT][4];
+        float lmax = 0.f;
+        const float s_old = sscale[0];
+#pragma unroll
+        for (int J = 0; J < RT; ++J) {
+          const int r = 16 * (sw * RT + J) + lane % 16;
+          const int8_t* crow = &stage[r * SP + 4 * (lane / 16)];
+#pragma unroll
+          for (int I = 0; I < CT; ++I) {
+            float gc[4];
+            if constexpr (DIAG) {
+              const float4 q4 = *reinterpret_cast<const float4*>(&gam[slot][16 * I + 4 * (lane / 16)]);
+              gc[0] = q4.x; gc[1] = q4.y; gc[2] = q4.z; gc[3] = q4.w;
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) gc[v] = gam[slot][0];
+            }
+            const uint32_t cw = *reinterpret_cast<const uint32_t*>(&crow[16 * I]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float S = (float)(int)(int8_t)(cw >> (8 * v)) * s_old;
+              x[J][I][v] = fmaf(gc[v], S, (float)acc[J][I][v] * sc);
+              lmax = fmaxf(lmax, fabsf(x[J][I][v]));
+            }
+          }
+        }
+        float sh = s_old;
+        if constexpr (XB) {
+          lmax = wave_max(lmax);
+          if (lane == 0) hmax[sw] = lmax;
+          __syncthreads();               // every state wave has read the old scale
+          sh = fmaxf(fmaxf(hmax[0], hmax[1]), fmaxf(hmax[2], hmax[3])) / QMAX;
+          if constexpr (S16) sh = scale_from16(scale_to16(sh, a.sfmt), a.sfmt);
+          if (sw == 0 && lane == 0) sscale[0] = sh;
+        }
+        const float inv = inv_scale(sh);
+#pragma unroll
+        for (int J = 0; J < RT; ++J) {
+          const int r = 16 * (sw * RT + J) + lane % 16;
+          int8_t* crow = &stage[r * SP + 4 * (lane / 16)];
+#pragma unroll
+          for (int I = 0; I < CT; ++I) {
+            uint32_t nw = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) nw |= (uint32_t)(rne_code(x[J][I][v], inv, QMAX) & 0xFF) << (8 * v);
+            *reinterpret_cast<uint32_t*>(&crow[16 * I]) = nw;
+          }
+        }
+        __syncthreads();
+        continue;
+      }
       const int tpg = g / 16;            // tiles per group (an aligned power of two)
 #pragma unroll
       for (int J = 0; J < RT; ++J) {
@@ -315,7 +384,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
     }
     ocodes[idx] = word;
   }
-  if constexpr (POLICY == POL_DYNAMIC) {
+  if constexpr (POLICY == POL_DYNAMIC && HEAD) {
+    if (tid == 0) {
+      if constexpr (S16)
+        reinterpret_cast<uint16_t*>(a.scales)[h] = (uint16_t)scale_to16(sscale[0], a.sfmt);
+      else
+        a.scales[h] = sscale[0];
+    }
+  } else if constexpr (POLICY == POL_DYNAMIC) {
     uint16_t* out16 = reinterpret_cast<uint16_t*>(a.scales);
     for (int idx = tid; idx < DV * ng; idx += 512) {
       if constexpr (S16)   // already a value of the format: the conversion is exact
@@ -333,10 +409,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int bits, int dk, int dv, int po
   const dim3 grid(a.n_heads), block(512);
 #define LSQ_PF(B, DK, DV, P, G)                                                                   \
   if (bits == B && dk == DK && dv == DV && policy == P && diag == G) {                           \
-    if (a.sfmt == dev::SFMT_F32)                                                                 \
-      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, false>), grid, block, 0, s, a);   \
+    const bool s16 = a.sfmt != dev::SFMT_F32, head = a.group == 0;                               \
+    if (!s16 && !head)                                                                           \
+      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, false, false>), grid, block, 0, s, a); \
+    else if (s16 && !head)                                                                       \
+      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, true, false>), grid, block, 0, s, a); \
+    else if (!s16)                                                                               \
+      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, false, true>), grid, block, 0, s, a); \
     else                                                                                         \
-      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, true>), grid, block, 0, s, a);    \
+      hipLaunchKernelGGL((dev::prefill_kernel<B, DK, DV, P, G, true, true>), grid, block, 0, s, a); \
     return hipGetLastError();                                                                    \
   }
 #define LSQ_PF_PG(B, DK, DV) \

@@ -186,7 +186,7 @@ def _alloc_all(cfg):
 
 @pytest.mark.parametrize("change", [
     dict(delta=1), dict(policy=lsq.POLICY_YOKED), dict(bits=32, group=1, policy=lsq.POLICY_NONE),
-    dict(dv=32), dict(dv=256), dict(lrb_rank=2), dict(group=0),
+    dict(dv=32), dict(dv=256), dict(lrb_rank=2),
 ])
 def test_prefill_rejects_unsupported_handles(change):
     base = dict(batch=1, heads=2, dk=128, dv=128, bits=4, group=32, policy=lsq.POLICY_DYNAMIC)

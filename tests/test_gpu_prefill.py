@@ -7,7 +7,7 @@ own round-half-even requantisation), so the codes and scales are held bit for
 bit, free-running over every chunk of the prompt, not teacher-forced.
 Cases: INT4/INT8, Dk and Dv 64/128, dynamic and persistent scales, scalar and
 diagonal decay, prompts that end mid-chunk, single tokens, the group sizes,
-binary16 and bfloat16 scales,
+binary16 and bfloat16 scales, one scale per head,
 a prompt split over several calls, a decode step after a prefill, and the
 full-size workload (batch 64 x 16 heads, 4096 tokens) on sampled heads.
 """
@@ -122,6 +122,33 @@ def test_prefill_16bit_scales(bits, pol, fmt, dc, group):
     st.prefill(dg["k"], dg["v"], dg["alpha"], dg["beta"])
     torch.cuda.synchronize()
     _check(cfg, st, before, dn, str(cfg))
+
+
+@pytest.mark.parametrize("bits,pol,dc", [
+    (b, p, dc)
+    for b in (4, 8)
+    for p in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+    for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)])
+def test_prefill_one_scale_per_head(bits, pol, dc):
+    """group 0: a dynamic head scale is taken over all of the head's X at every
+    chunk (the state waves meet at one more barrier), a frozen one is kept;
+    codes and scales bit for bit, then a decode step from the prefilled state."""
+    for dk, dv in ((128, 128), (64, 64)):
+        cfg = lsq.LsqConfig(batch=1, heads=3, dk=dk, dv=dv, bits=bits, group=0, policy=pol,
+                            delta=0, decay=dc)
+        st = _state(cfg)
+        before = snapshot(st)
+        dg, dn = _inputs(_recipe(dc), cfg.n, dk, dv, 150, seed=17)
+        st.prefill(dg["k"], dg["v"], dg["alpha"], dg["beta"])
+        torch.cuda.synchronize()
+        _check(cfg, st, before, dn, str(cfg))
+    d2g, d2n = _inputs(_recipe(dc), cfg.n, cfg.dk, cfg.dv, 1, seed=18, t0=150)
+    before = snapshot(st)
+    o = st.step(d2g["q"][0], d2g["k"][0], d2g["v"][0], d2g["alpha"][0], d2g["beta"][0])
+    rep = compare_step(ocfg_of(cfg, step=150), before,
+                       tuple(d2n[x][0] for x in ("q", "k", "v", "alpha", "beta")), snapshot(st),
+                       o.cpu().numpy())
+    assert rep.ok, str(rep)
 
 
 def test_prefill_from_zero_state_and_empty_prompt():
