@@ -51,6 +51,38 @@ __device__ __forceinline__ int rne_code(float x, float inv, float qmax) {
   return (int)(__float_as_uint(t) - __float_as_uint(kMagic));
 }
 
+// max of x over the four lanes l, l^16, l^32, l^48 (the lanes that hold one
+// state row): the gfx950 row-swap instructions, no LDS round trip.
+__device__ __forceinline__ float max_across_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// fl(m / qmax) for qmax = 7 (INT4) or 127 (INT8): the product with fl(1/qmax),
+// its exact residual and one corrective fma.  Equal to the IEEE quotient for
+// every finite m >= 0 (checked over all finite floats for both divisors);
+// m = +inf gives NaN, which the caller's range check sends to IEEE division.
+template <int BITS>
+__device__ __forceinline__ float div_qmax(float m) {
+  constexpr float QM = BITS == 4 ? 7.f : 127.f;
+  constexpr float C = 1.f / QM;
+  const float q = m * C;
+  const float r = fmaf(-q, QM, m);
+  return fmaf(r, C, q);
+}
+
+// fl(1/s) for s in [2^-126, 2^126): v_rcp_f32 and one Newton step (the
+// decode step's reciprocal without its out-of-range branch).
+__device__ __forceinline__ float rcp_newton(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = fmaf(-s, r0, 1.0f);
+  return fmaf(e, r0, r0);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -85,6 +117,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   __shared__ float wmax[2][4];                          // per operand wave block absmax
   __shared__ float opscale[2][2];                       // s_V, s_K
   __shared__ float hmax[4];                             // per state wave |X| max (HEAD)
+  constexpr int OPC = 128 + DV;                          // staged operand columns: K at c, V at 128 + row
+  __shared__ float colbuf[kChunk * OPC];                // fp32 operand columns of the next chunk [token][column]
   constexpr bool XB = HEAD && POLICY == POL_DYNAMIC;    // the extra barrier per chunk
 
   // ---- the head's packed state -> LDS codes and scales.  The state stays
@@ -120,96 +154,114 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
   const bool krole = wave < KW, vrole = wave >= 2 && wave < 2 + VW;
   const bool swave = wave >= 4;
   const unsigned ut = threadIdx.x;       // unsigned lane offset: scalar base + vector offset loads
-  float col[kChunk];                     // operand column of the chunk in flight
-  float gh = 1.f;                        // its gamma^C (K side)
 
-  // Both roles run nchunk + 2 iterations with one barrier each, in two
-  // separate loops (wave-uniform branch) so that neither holds the other's
-  // registers.
-  if (!swave) {
+  // One operand role (K side or V side), as a loop of its own: nchunk + 2
+  // iterations with one barrier each.  The reads of the next chunk to build
+  // are issued one iteration before they are used, so that their HBM latency
+  // overlaps a whole iteration; every read is unconditional within the loop
+  // (no register copy of a read value, which would wait for all reads in
+  // flight).
+  auto operand_loop = [&](auto kside) {
+    constexpr bool K = decltype(kside)::value;
+    constexpr bool TOK = !(K && DIAG);   // a per-token scalar (scalar decay, beta): lane t, token t
+    const int col_c = K ? tid : tid - 128;
+    float v0[kChunk], v1[TOK ? 1 : kChunk];
+    float pl = 0.f;
+    float gh = 1.f;                      // gamma^C of the chunk last built (K side)
+    // reads of chunk p (p < nchunk); a short chunk re-reads its last token
+    auto read_chunk = [&](int p) {
+      const int c0 = p * kChunk;
+      const int tm = min(kChunk, a.T - c0) - 1;
+      const int64_t row0 = (int64_t)c0 * nh + h;
+      const int64_t s0 = nh * (K ? DK : DV);
+      const float* r = K ? a.k + row0 * DK : a.v + row0 * DV - 128;
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        v0[t] = r[ut];
+        if (t < tm) r += s0;
+      }
+      if constexpr (!TOK) {
+        const float* ra = a.alpha + row0 * DK;
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+          v1[t] = ra[ut];
+          if (t < tm) ra += s0;
+        }
+      } else {
+        pl = (K ? a.alpha : a.beta)[row0 + (int64_t)min(lane, tm) * nh];
+      }
+    };
+    float* mycol = &colbuf[tid];         // this thread's operand column, token stride OPC
+    if (nchunk > 0) read_chunk(0);
     for (int i = -2; i < nchunk; ++i) {
       // ---- (a) quantise chunk i+1's columns with the posted block maxima
       const int q = i + 1;
-      if (q >= 0 && q < nchunk && (krole || vrole)) {
+      if (q >= 0 && q < nchunk) {
         const int slot = q & 1;
-        float mk = wmax[slot][0], mv = wmax[slot][2];
-        if (KW > 1) mk = fmaxf(mk, wmax[slot][1]);
-        if (VW > 1) mv = fmaxf(mv, wmax[slot][3]);
-        const float s_v = mv / 127.f, s_k = mk / 127.f;
-        const float inv = inv_scale(krole ? s_k : s_v);
-        int8_t* dst = krole ? &kt[slot][tid * kOpRow] : &vt[slot][(tid - 128) * kOpRow];
+        float m = wmax[slot][K ? 0 : 2];
+        if ((K ? KW : VW) > 1) m = fmaxf(m, wmax[slot][K ? 1 : 3]);
+        const float sq = m / 127.f;
+        const float inv = inv_scale(sq);
+        int8_t* dst = K ? &kt[slot][col_c * kOpRow] : &vt[slot][col_c * kOpRow];
 #pragma unroll
         for (int t4 = 0; t4 < kChunk / 4; ++t4) {
           uint32_t w = 0;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) w |= (uint32_t)(rne_code(col[4 * t4 + b], inv, 127.f) & 0xFF) << (8 * b);
+          for (int b = 0; b < 4; ++b)
+            w |= (uint32_t)(rne_code(mycol[(4 * t4 + b) * OPC], inv, 127.f) & 0xFF) << (8 * b);
           reinterpret_cast<uint32_t*>(dst)[t4] = w;
         }
-        if (krole) gam[slot][tid] = gh;
-        if (tid == 0) {
-          opscale[slot][0] = s_v;
-          opscale[slot][1] = s_k;
-        }
+        if constexpr (K) gam[slot][col_c] = gh;
+        if (col_c == 0) opscale[slot][K ? 1 : 0] = sq;
       }
-      // ---- (b) read chunk i+2 and build its operand columns
+      // ---- (b) build chunk i+2's operand columns from its reads (into LDS,
+      // over the values (a) has just taken), then read chunk i+3 (the last
+      // chunk again when there is none: its lines are still in the cache)
       const int p = i + 2;
-      if (p < nchunk && (krole || vrole)) {
-        const int c0 = p * kChunk;
-        const int tc = min(kChunk, a.T - c0);
-        const int64_t row0 = (int64_t)c0 * nh + h;
-        float v0[kChunk], v1[kChunk];
-        float pl = 0.f;                  // per-token scalar (scalar decay, beta): lane t holds token t
-        {
-          const float* r0 = krole ? a.k + row0 * DK : a.v + row0 * DV - 128;
-          const int64_t s0 = krole ? nh * DK : nh * DV;
-          if (tc == kChunk) {            // full chunk: row pointers advance by one token
-            const float* r = r0;
-#pragma unroll
-            for (int t = 0; t < kChunk; ++t, r += s0) v0[t] = r[ut];
-          } else {                       // a short chunk re-reads its last token
-#pragma unroll
-            for (int t = 0; t < kChunk; ++t) v0[t] = r0[min(t, tc - 1) * s0 + ut];
-          }
-          if (krole && DIAG) {
-            const float* ra = a.alpha + row0 * DK;
-            if (tc == kChunk) {
-              const float* r = ra;
-#pragma unroll
-              for (int t = 0; t < kChunk; ++t, r += nh * DK) v1[t] = r[ut];
-            } else {
-#pragma unroll
-              for (int t = 0; t < kChunk; ++t) v1[t] = ra[min(t, tc - 1) * nh * DK + ut];
-            }
-          } else {
-            const float* rs = krole ? a.alpha : a.beta;
-            pl = rs[row0 + (int64_t)min(lane, tc - 1) * nh];
-          }
-        }
+      if (p < nchunk) {
+        const int tc = min(kChunk, a.T - p * kChunk);
         float cmax = 0.f;
-        if (krole) {
+        if constexpr (K) {
           float acc = 1.f;               // Gamma->: product of the later tokens' decays
 #pragma unroll
           for (int t = kChunk - 1; t >= 0; --t) {
             const bool in = t < tc;
             const float dec =
-                DIAG ? v1[t] : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), t));
-            col[t] = in ? acc * v0[t] : 0.f;
+                TOK ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), t)) : v1[TOK ? 0 : t];
+            const float c = in ? acc * v0[t] : 0.f;
             acc = in ? acc * dec : acc;
-            cmax = fmaxf(cmax, fabsf(col[t]));
+            mycol[t * OPC] = c;
+            cmax = fmaxf(cmax, fabsf(c));
           }
           gh = acc;
         } else {
 #pragma unroll
           for (int t = 0; t < kChunk; ++t) {
             const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pl), t));
-            col[t] = t < tc ? b * v0[t] : 0.f;
-            cmax = fmaxf(cmax, fabsf(col[t]));
+            const float c = t < tc ? b * v0[t] : 0.f;
+            mycol[t * OPC] = c;
+            cmax = fmaxf(cmax, fabsf(c));
           }
         }
         cmax = wave_max(cmax);
         if (lane == 0) wmax[p & 1][wave] = cmax;
+        // the next reads stay below this chunk's last use of v0, v1 and pl,
+        // so that they land in the same registers
+        asm volatile("" ::: "memory");
+        read_chunk(min(p + 1, nchunk - 1));
       }
       if constexpr (XB) __syncthreads();   // the state waves' head maximum
+      __syncthreads();
+    }
+  };
+
+  if (krole) {
+    operand_loop(std::true_type{});
+  } else if (vrole) {
+    operand_loop(std::false_type{});
+  } else if (!swave) {                   // no operand role at this shape: the barriers only
+    for (int i = -2; i < nchunk; ++i) {
+      if constexpr (XB) __syncthreads();
       __syncthreads();
     }
   } else {
@@ -324,11 +376,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
             x[I][v] = fmaf(gc[v], S, (float)acc[J][I][v] * sc);
           }
         }
+        float m[CT];                     // group maxima (dynamic)
         if constexpr (POLICY == POL_DYNAMIC) {
           // group absmax: the tile's four columns in the lane, the group's
           // tiles by butterflies (static indices), then the four lanes that
           // hold the row (l%16 fixed)
-          float m[CT];
 #pragma unroll
           for (int I = 0; I < CT; ++I)
             m[I] = fmaxf(fmaxf(fabsf(x[I][0]), fabsf(x[I][1])), fmaxf(fabsf(x[I][2]), fabsf(x[I][3])));
@@ -343,21 +395,46 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillArgs a) {
             }
           }
 #pragma unroll
+          for (int I = 0; I < CT; ++I) m[I] = max_across_rows(m[I]);
+#pragma unroll
           for (int I = 0; I < CT; ++I) {
-            m[I] = fmaxf(m[I], __shfl_xor(m[I], 16));
-            m[I] = fmaxf(m[I], __shfl_xor(m[I], 32));
-            s[I] = m[I] / QMAX;
+            s[I] = div_qmax<BITS>(m[I]);
             // a 16-bit format: the stored value forms the codes
             if constexpr (S16) s[I] = scale_from16(scale_to16(s[I], a.sfmt), a.sfmt);
-            if (lane < 16 && (I % tpg) == 0) sscale[r * ng + (16 * I) / g] = s[I];
+          }
+        }
+        // reciprocals of every tile's scale; lanes holding a zero, tiny, huge
+        // or non-finite scale (or group maximum) redo theirs with IEEE
+        // division, in one branch for all the tiles
+        float inv[CT];
+        bool slow = false;
+#pragma unroll
+        for (int I = 0; I < CT; ++I) {
+          inv[I] = rcp_newton(s[I]);
+          slow = slow || !(s[I] >= 0x1p-126f && s[I] < 0x1p126f);
+        }
+        if (__builtin_expect(slow, 0)) {
+#pragma unroll
+          for (int I = 0; I < CT; ++I) {
+            if constexpr (POLICY == POL_DYNAMIC) {
+              s[I] = m[I] / QMAX;
+              if constexpr (S16) s[I] = scale_from16(scale_to16(s[I], a.sfmt), a.sfmt);
+            }
+            inv[I] = inv_scale(s[I]);
+          }
+        }
+        if constexpr (POLICY == POL_DYNAMIC) {
+          if (lane < 16) {
+#pragma unroll
+            for (int I = 0; I < CT; ++I)
+              if ((I % tpg) == 0) sscale[r * ng + (16 * I) / g] = s[I];
           }
         }
 #pragma unroll
         for (int I = 0; I < CT; ++I) {
-          const float inv = inv_scale(s[I]);
           uint32_t nw = 0;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) nw |= (uint32_t)(rne_code(x[I][v], inv, QMAX) & 0xFF) << (8 * v);
+          for (int v = 0; v < 4; ++v) nw |= (uint32_t)(rne_code(x[I][v], inv[I], QMAX) & 0xFF) << (8 * v);
           *reinterpret_cast<uint32_t*>(&crow[16 * I]) = nw;
         }
       }
