@@ -94,6 +94,32 @@ def test_step_matches_oracle(bits, dk, pol, rnd, dl, dc):
     assert rep.failed == 0 and rep.o_differ == 0, str(rep)
 
 
+MULTI = [(bits, dk, pol, rnd, dl, dc)
+         for bits in (4, 8)
+        for dk in (128, 64)
+        for pol in (lsq.POLICY_DYNAMIC, lsq.POLICY_PERSISTENT)
+        for rnd in (lsq.ROUND_RNE, lsq.ROUND_BDR)
+        for dl in (0, 1)
+        for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc", MULTI)
+def test_multi_row_waves_match_oracle(bits, dk, pol, rnd, dl, dc):
+    """States of 1024 heads: the launch shape of few-head states, two waves per
+    head with four row-iterations each, so that every wave walks its rows with
+    the next row's loads in flight (the small states above take one
+    row-iteration per wave).  Dv leaves a ragged last row-iteration."""
+    group = 32 if bits == 4 else 64
+    dv = 120 if dk == 128 else 250
+    cfg = lsq.LsqConfig(batch=32, heads=32, dk=dk, dv=dv, bits=bits, group=min(group, dk),
+                        policy=pol, rounding=rnd, delta=dl, decay=dc)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=3, recipe=recipe)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)
+
+
 ZD = [(bits, dk, pol, dl, dc)
       for bits in (4, 8)
       for dk in (128, 64)
