@@ -125,6 +125,26 @@ __device__ __forceinline__ void store_lds(float* dst, const float (&src)[N]) {
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 
+// One or two consecutive floats (a lane's share of a staged vector).
+template <int N>
+__device__ __forceinline__ void load_cols(float (&d)[N], const float* __restrict__ src) {
+  if constexpr (N == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(src);
+    d[0] = t.x;
+    d[1] = t.y;
+  } else {
+    d[0] = src[0];
+  }
+}
+template <int N>
+__device__ __forceinline__ void store_cols(float* dst, const float (&v)[N]) {
+  if constexpr (N == 2)
+    *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+  else
+    dst[0] = v[0];
+}
+
+
 // x & m, opaque to the optimiser: keeps "(w >> 8b) & 0xFF -> float" as one
 // v_cvt_f32_ubyte<b> per element instead of a bit-field extract plus a convert.
 __device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
@@ -154,6 +174,55 @@ __device__ __forceinline__ void fma_ru8(float* d, const float* a, float b, float
         "=&v"(d[6]), "=&v"(d[7])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
         "v"(b), "v"(c));
+}
+
+// d[i] = d[i] * b0 + c (i = 0..15) and d[i] * b1 + c (i = 16..31), rounded toward
+// +infinity, in place: the 32 round-up candidates of a lane's row under one
+// switch of the MODE register's single-precision rounding field (the block-of-
+// eight form switches four times per row).
+__device__ __forceinline__ void fma_ru32(float* d, float b0, float b1, float c) {
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 1\n\t"
+      "s_nop 1\n\t"
+      "v_fma_f32 %0, %0, %32, %34\n\t"
+      "v_fma_f32 %1, %1, %32, %34\n\t"
+      "v_fma_f32 %2, %2, %32, %34\n\t"
+      "v_fma_f32 %3, %3, %32, %34\n\t"
+      "v_fma_f32 %4, %4, %32, %34\n\t"
+      "v_fma_f32 %5, %5, %32, %34\n\t"
+      "v_fma_f32 %6, %6, %32, %34\n\t"
+      "v_fma_f32 %7, %7, %32, %34\n\t"
+      "v_fma_f32 %8, %8, %32, %34\n\t"
+      "v_fma_f32 %9, %9, %32, %34\n\t"
+      "v_fma_f32 %10, %10, %32, %34\n\t"
+      "v_fma_f32 %11, %11, %32, %34\n\t"
+      "v_fma_f32 %12, %12, %32, %34\n\t"
+      "v_fma_f32 %13, %13, %32, %34\n\t"
+      "v_fma_f32 %14, %14, %32, %34\n\t"
+      "v_fma_f32 %15, %15, %32, %34\n\t"
+      "v_fma_f32 %16, %16, %33, %34\n\t"
+      "v_fma_f32 %17, %17, %33, %34\n\t"
+      "v_fma_f32 %18, %18, %33, %34\n\t"
+      "v_fma_f32 %19, %19, %33, %34\n\t"
+      "v_fma_f32 %20, %20, %33, %34\n\t"
+      "v_fma_f32 %21, %21, %33, %34\n\t"
+      "v_fma_f32 %22, %22, %33, %34\n\t"
+      "v_fma_f32 %23, %23, %33, %34\n\t"
+      "v_fma_f32 %24, %24, %33, %34\n\t"
+      "v_fma_f32 %25, %25, %33, %34\n\t"
+      "v_fma_f32 %26, %26, %33, %34\n\t"
+      "v_fma_f32 %27, %27, %33, %34\n\t"
+      "v_fma_f32 %28, %28, %33, %34\n\t"
+      "v_fma_f32 %29, %29, %33, %34\n\t"
+      "v_fma_f32 %30, %30, %33, %34\n\t"
+      "v_fma_f32 %31, %31, %33, %34\n\t"
+      "s_nop 1\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0"
+      : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]), "+v"(d[7]),
+        "+v"(d[8]), "+v"(d[9]), "+v"(d[10]), "+v"(d[11]), "+v"(d[12]), "+v"(d[13]), "+v"(d[14]), "+v"(d[15]),
+        "+v"(d[16]), "+v"(d[17]), "+v"(d[18]), "+v"(d[19]), "+v"(d[20]), "+v"(d[21]), "+v"(d[22]), "+v"(d[23]),
+        "+v"(d[24]), "+v"(d[25]), "+v"(d[26]), "+v"(d[27]), "+v"(d[28]), "+v"(d[29]), "+v"(d[30]), "+v"(d[31])
+      : "v"(b0), "v"(b1), "v"(c));
 }
 
 // d[i] = (a[i] * b + e[i]) + c, both operations rounded toward -infinity:
@@ -510,6 +579,11 @@ struct Lane {
   HeadPtrs H;         // this head's rows
   float alpha_s, beta;
   float alpha_hi;     // max |alpha_c| over the head (the scalar decay's |alpha|)
+  // max |alpha_c| <= 1 - 2^-20: then fl(qmax fl(s |alpha_c|)) fl(1/s) < qmax for
+  // every zero or normal scale s (three roundings of relative size <= 2^-22
+  // cannot make up a 2^-20 deficit, subnormal intermediates included), so the
+  // per-row test of the round-up candidate's range is known to pass
+  bool decay_in_range;
   uint32_t Kf[REG_MASKS ? NW : 1], Kx[REG_MASKS ? NW : 1], K1[REG_MASKS ? NW : 1];
 };
 
@@ -698,7 +772,12 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       if constexpr (BDR) {
         const float inv_w = __uint_as_float(fbits(inv) ^ wsign);
         float tu[8];
-        fma_ru8(tu, spb, inv_w, mu);                   // ceil(z') + MQ
+        if constexpr (ONE_PASS) {
+          fma_ru8(tu, spb, inv_w, mu);                 // ceil(z') + MQ
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) tu[i] = spb[i];  // already ceil(z') + MQ (fma_ru32)
+        }
         if constexpr (KZ) {
           // no update direction where k_c = 0: the candidate is the clamp's floor
           float kb[8];
@@ -750,13 +829,16 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       for (int h = 0; h < GPL; ++h) inv[h] = inv_scale(snew[h]);
       bool in_range = false;
       if constexpr (BDR) {
-        bool ok = true;
+        in_range = L.decay_in_range;
+        if (!in_range) {
+          bool ok = true;
 #pragma unroll
-        for (int h = 0; h < GPL; ++h) {
-          const float mq = F::QMAX * fabsf(in.s[h] * L.alpha_hi);
-          ok = ok && fmaf(mq, inv[h], -F::QMAX) <= 0.f;
+          for (int h = 0; h < GPL; ++h) {
+            const float mq = F::QMAX * fabsf(in.s[h] * L.alpha_hi);
+            ok = ok && fmaf(mq, inv[h], -F::QMAX) <= 0.f;
+          }
+          in_range = __all(ok);
         }
-        in_range = __all(ok);
       }
       auto pass = [&](auto in_range_t) {
 #pragma unroll
@@ -868,13 +950,20 @@ __device__ __forceinline__ void row_loop(const StepArgs& a, Lane<BITS, DK, POLIC
       // within it, so the median is min(tz, MQ + qmax) there as well.
       bool in_range = false;
       if constexpr (BDR && POLICY == POL_PERSISTENT) {
-        bool ok = true;
+        in_range = L.decay_in_range;
+        if (!in_range) {
+          bool ok = true;
 #pragma unroll
-        for (int h = 0; h < GPL; ++h) {
-          const float mq = F::QMAX * fabsf(in.s[h] * L.alpha_hi);
-          ok = ok && fmaf(mq, inv[h], -F::QMAX) <= 0.f;
+          for (int h = 0; h < GPL; ++h) {
+            const float mq = F::QMAX * fabsf(in.s[h] * L.alpha_hi);
+            ok = ok && fmaf(mq, inv[h], -F::QMAX) <= 0.f;
+          }
+          in_range = __all(ok);
         }
-        in_range = __all(ok);
+      }
+      if constexpr (BDR) {   // the row's round-up candidates, in place of S'
+        fma_ru32(sp, __uint_as_float(fbits(inv[0]) ^ wsign),
+                 __uint_as_float(fbits(inv[GPL - 1]) ^ wsign), mu);
       }
       if (in_range) {
 #pragma unroll
@@ -973,9 +1062,20 @@ void step_kernel(StepArgs a) {
   __shared__ float4 vec4[4 * P::WAVE_FLOATS / 4];
   float* vec = reinterpret_cast<float*>(vec4);
   L.vbase = (threadIdx.x >> 6) * P::WAVE_FLOATS;
-  float kk[EPL], qq[EPL];
-  load_f32(kk, a.k + (size_t)L.h * DK + L.col0);
-  load_f32(qq, a.q + (size_t)L.h * DK + L.col0);
+  // The head's vectors are staged by all 64 lanes, DK/64 columns each: a
+  // lane loads, transforms and stores only its own columns (sc, sc+1), at
+  // their place in the padded chunk layout.  Directional rounding also needs
+  // the sign bits of the lane's own 32 row columns (kk) for its orientation
+  // masks.
+  constexpr int CPL = DK / 64;
+  static_assert(CPL == 1 || CPL == 2, "staging takes one or two columns per lane");
+  const int sc = lane * CPL;
+  const int soff = L.vbase + (sc / EPL) * P::CHUNK + (sc % EPL);
+  float ks[CPL], qs[CPL];
+  load_cols<CPL>(ks, a.k + (size_t)L.h * DK + sc);
+  load_cols<CPL>(qs, a.q + (size_t)L.h * DK + sc);
+  float kk[BDR ? EPL : 4];
+  if constexpr (BDR) load_f32(kk, a.k + (size_t)L.h * DK + L.col0);
   // The wave's first row (codes, scale, v) is requested before the head's
   // vectors arrive, so that the two loads' latencies overlap, except in the
   // persistent-BDR instances where holding that row through the set-up below
@@ -997,23 +1097,26 @@ void step_kernel(StepArgs a) {
   L.alpha_s = DIAG ? 1.f : a.alpha[L.h];
   L.alpha_hi = fabsf(L.alpha_s);
   L.beta = a.beta[L.h];
-  const bool writer = L.lr == 0;         // one lane per column chunk fills LDS
+  const bool writer = L.lr == 0;         // one lane per column chunk fills the INT8 masks
   if constexpr (DIAG) {
-    float aa[EPL];
-    load_f32(aa, a.alpha + (size_t)L.h * DK + L.col0);
-    if (writer) store_lds(vec + L.vbase + 2 * P::VSTRIDE + L.lc * P::CHUNK, aa);
-    float am = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) am = fmaxf(am, fabsf(aa[e]));
-    L.alpha_hi = group_max(am, LPR);
+    float as[CPL];
+    load_cols<CPL>(as, a.alpha + (size_t)L.h * DK + sc);
+    store_cols<CPL>(vec + soff + 2 * P::VSTRIDE, as);
+    float am = fabsf(as[0]);
+    if constexpr (CPL == 2) am = fmaxf(am, fabsf(as[1]));
+    am = group_max(am, 16);                              // within each 16-lane row
+    am = fmaxf(am, __shfl_xor(am, 16));
+    L.alpha_hi = fmaxf(am, __shfl_xor(am, 32));          // over the head's DK columns
   }
+
+  L.decay_in_range = __builtin_amdgcn_readfirstlane(L.alpha_hi <= 0x1.ffffep-1f ? 1 : 0) != 0;
 
   bool kzero = false;
   if constexpr (BDR) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) kzero |= (ks[i] == 0.f);
     // Oriented frame: per column rho_c = sign(k_c) (the sign bit, so -0 counts
     // as negative).  Kf marks, nibble- or byte-wise, the negated columns.
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) kzero |= (kk[e] == 0.f);
     // v_perm selector 9 (11) replicates the sign bit of the second (first) operand
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
@@ -1044,21 +1147,17 @@ void step_kernel(StepArgs a) {
       }
     }
     if constexpr (POLICY == POL_YOKED) {
-      if (writer) {
-        store_lds(vec + L.vbase + 3 * P::VSTRIDE + L.lc * P::CHUNK, kk);
-        store_lds(vec + L.vbase + 4 * P::VSTRIDE + L.lc * P::CHUNK, qq);
-      }
+      store_cols<CPL>(vec + soff + 3 * P::VSTRIDE, ks);
+      store_cols<CPL>(vec + soff + 4 * P::VSTRIDE, qs);
     }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      qq[e] = __uint_as_float(fbits(qq[e]) ^ (fbits(kk[e]) & 0x80000000u));
-      kk[e] = fabsf(kk[e]);
+    for (int i = 0; i < CPL; ++i) {
+      qs[i] = __uint_as_float(fbits(qs[i]) ^ (fbits(ks[i]) & 0x80000000u));
+      ks[i] = fabsf(ks[i]);
     }
   }
-  if (writer) {
-    store_lds(vec + L.vbase + 0 * P::VSTRIDE + L.lc * P::CHUNK, kk);
-    store_lds(vec + L.vbase + 1 * P::VSTRIDE + L.lc * P::CHUNK, qq);
-  }
+  store_cols<CPL>(vec + soff + 0 * P::VSTRIDE, ks);
+  store_cols<CPL>(vec + soff + 1 * P::VSTRIDE, qs);
   // LDS accesses of one wave execute in order; the barrier keeps the compiler
   // from moving reads of the staged vectors above these writes.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
