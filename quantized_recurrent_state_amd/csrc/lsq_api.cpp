@@ -137,6 +137,11 @@ void sizes_of(const lsq_config& c, size_t (&sz)[kBuffers]) {
   if (c.lrb_rank > 0) sz[4] = (size_t)n_heads(c) * c.lrb_rank * (c.dv + 2 * (size_t)c.dk) * 4;
 }
 
+// Wave target of the plain quantised step (see launch_one_step).
+#ifndef LSQ_LEAN_WAVES
+#define LSQ_LEAN_WAVES 4096
+#endif
+
 // Launch geometry: one wave per (head, slice of nit row-iterations); slices
 // shrink until there are at least `target` waves.  The default, 8192 (256 CUs
 // x 32 waves), keeps every SIMD busy when a wave's rows are memory-heavy.
@@ -192,14 +197,16 @@ lsq_status launch_one_step(lsq_state* st, const float* q, const float* k, const 
   }
   // The plain quantised step (no bypass buffer, no fp32 reference) on a state
   // of few heads: each wave stages its head's vectors before its first row, so
-  // fewer, longer waves (2048: two per SIMD, each with the next row in flight)
-  // pay that set-up less often.  Measured on 1024 heads with a diagonal decay,
-  // 12.6 -> 10.7 us per step; 4096 dynamic-scale heads 28.7 -> 27.6 us; a state
-  // of more heads than that already runs one wave per head either way.
+  // fewer, longer waves (4096: four per SIMD, each with the next row in flight)
+  // pay that set-up less often.  Measured on 1024 heads with a diagonal decay
+  // (median launch): 13.6 us at 1024 waves, 10.9 at 2048, 10.4 at 4096, 10.5 at
+  // 8192 and 16384; 4096 dynamic-scale heads and 8192 Mamba-2-style heads are
+  // within 2% from 1024 to 8192 waves; a state of more heads than that already
+  // runs one wave per head either way.
   const bool lean = c.bits != 32 && c.lrb_rank == 0 && c.policy != LSQ_POLICY_YOKED &&
                     c.rounding != LSQ_ROUND_BDR_A && c.rounding != LSQ_ROUND_BDR_B &&
                     !(c.group == 0 && c.policy == LSQ_POLICY_DYNAMIC);
-  choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves, lean ? 2048 : 8192);
+  choose_slices(c, &a.nit, &a.waves_per_head, &a.total_waves, lean ? LSQ_LEAN_WAVES : 8192);
   // a state of 512 MiB or more does not stay in the 256 MB Infinity Cache
   // between steps: its code loads take the non-temporal hint
   a.nt_loads = (size_t)n_heads(c) * c.dv * c.dk * (size_t)c.bits / 8 >= ((size_t)512 << 20);

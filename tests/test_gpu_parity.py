@@ -105,13 +105,14 @@ MULTI = [(bits, dk, pol, rnd, dl, dc)
 
 @pytest.mark.parametrize("bits,dk,pol,rnd,dl,dc", MULTI)
 def test_multi_row_waves_match_oracle(bits, dk, pol, rnd, dl, dc):
-    """States of 1024 heads: the launch shape of few-head states, two waves per
-    head with four row-iterations each, so that every wave walks its rows with
-    the next row's loads in flight (the small states above take one
-    row-iteration per wave).  Dv leaves a ragged last row-iteration."""
+    """States of 2048 heads: the launch shape of few-head states (4096 waves),
+    two waves per head with four row-iterations each, so that every wave walks
+    its rows with the next row's loads in flight and reloads its first buffer
+    (the small states above take one row-iteration per wave).  Dv leaves a
+    ragged last row-iteration."""
     group = 32 if bits == 4 else 64
     dv = 120 if dk == 128 else 250
-    cfg = lsq.LsqConfig(batch=32, heads=32, dk=dk, dv=dv, bits=bits, group=min(group, dk),
+    cfg = lsq.LsqConfig(batch=64, heads=32, dk=dk, dv=dv, bits=bits, group=min(group, dk),
                         policy=pol, rounding=rnd, delta=dl, decay=dc)
     recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
     rep = _run_teacher_forced(cfg, steps=3, recipe=recipe)
