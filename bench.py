@@ -336,8 +336,9 @@ def measure_ceiling(dev, stream, gib: float, span_kib: int) -> dict:
     hint), and the in-place span walk of the decode step's own access pattern
     (one wave per span of span_kib KiB).  Best of five launches each, HIP events
     on the launch stream; GB/s counts bytes read plus bytes written.  Also the
-    VALU issue rate of fma, med3 and a four-and-four mix at four waves per SIMD
-    (lsq_probe_valu), in wave64 instructions per second."""
+    VALU issue rate of fma, med3, a four-and-four mix and seven more single
+    instruction kinds at four waves per SIMD (lsq_probe_valu), in wave64
+    instructions per second."""
     import torch
     import quantized_recurrent_state_amd as lsq
 
@@ -382,7 +383,10 @@ def measure_ceiling(dev, stream, gib: float, span_kib: int) -> dict:
     sink = torch.zeros(4, device=dev)
     wg, iters = 1024, 8192
     for name, form in (("fma", lsq.PROBE_VALU_FMA), ("med3", lsq.PROBE_VALU_MED3),
-                       ("mixed", lsq.PROBE_VALU_MIXED)):
+                       ("mixed", lsq.PROBE_VALU_MIXED), ("fmac", lsq.PROBE_VALU_FMAC),
+                       ("fma_mix", lsq.PROBE_VALU_FMA_MIX), ("lshl_or", lsq.PROBE_VALU_LSHL_OR),
+                       ("perm", lsq.PROBE_VALU_PERM), ("xad", lsq.PROBE_VALU_XAD),
+                       ("and", lsq.PROBE_VALU_AND), ("mul", lsq.PROBE_VALU_MUL)):
         run = lambda: lsq.lsq_probe_valu(form, wg, iters, sink, stream)
         run()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -63,9 +63,17 @@ lsq_status lsq_probe_span(const void* src, void* dst, size_t bytes, int32_t span
                           int32_t nontemporal, void* stream);
 
 typedef enum {
-  LSQ_PROBE_VALU_FMA = 0,    /* v_fma_f32, every operand a VGPR (the fast issue class) */
-  LSQ_PROBE_VALU_MED3 = 1,   /* v_med3_f32 (the slow issue class) */
-  LSQ_PROBE_VALU_MIXED = 2   /* four of each per iteration */
+  LSQ_PROBE_VALU_FMA = 0,      /* v_fma_f32, every operand a VGPR */
+  LSQ_PROBE_VALU_MED3 = 1,     /* v_med3_f32 */
+  LSQ_PROBE_VALU_MIXED = 2,    /* four of each per iteration */
+  /* one instruction each, written out in inline asm, every operand a VGPR: */
+  LSQ_PROBE_VALU_FMAC = 3,     /* v_fmac_f32, the accumulating two-operand fma */
+  LSQ_PROBE_VALU_FMA_MIX = 4,  /* v_fma_mix_f32 (a binary16 operand) */
+  LSQ_PROBE_VALU_LSHL_OR = 5,  /* v_lshl_or_b32 */
+  LSQ_PROBE_VALU_PERM = 6,     /* v_perm_b32 */
+  LSQ_PROBE_VALU_XAD = 7,      /* v_xad_u32 */
+  LSQ_PROBE_VALU_AND = 8,      /* v_and_b32 */
+  LSQ_PROBE_VALU_MUL = 9       /* v_mul_f32 */
 } lsq_probe_valu_form;
 
 /* VALU issue probe: the rate at which this part retires one instruction form
@@ -75,8 +83,10 @@ typedef enum {
  * waves); every lane runs `iters` iterations of eight independent chains of
  * the form, so one launch issues workgroups * 4 * iters * 8 wave64
  * instructions of it (1024 workgroups fill the chip's SIMDs four waves deep).
- * No memory is read; out (4 bytes) is written only if the chains' sum equals
- * a value they cannot produce, which keeps the compiler from removing them.
+ * The rates of the forms price a kernel's instruction mix.  No memory is
+ * read; out (4 bytes) is written only if the chains' sum equals a value they
+ * cannot produce (forms 0-2), which keeps the compiler from removing them
+ * (forms 3-9 are kept by their volatile asm and never write out).
  *   form        lsq_probe_valu_form
  *   workgroups  >= 1
  *   iters       >= 1

@@ -163,6 +163,8 @@ def lsq_probe_span(src, dst, nbytes: int, span_kib: int = 10, nontemporal: int =
 
 
 PROBE_VALU_FMA, PROBE_VALU_MED3, PROBE_VALU_MIXED = 0, 1, 2
+PROBE_VALU_FMAC, PROBE_VALU_FMA_MIX, PROBE_VALU_LSHL_OR, PROBE_VALU_PERM = 3, 4, 5, 6
+PROBE_VALU_XAD, PROBE_VALU_AND, PROBE_VALU_MUL = 7, 8, 9
 
 
 def lsq_probe_valu(form: int, workgroups: int, iters: int, out, stream=None) -> None:

@@ -529,8 +529,8 @@ lsq_status lsq_probe_span(const void* src, void* dst, size_t bytes, int32_t span
 
 lsq_status lsq_probe_valu(int32_t form, int32_t workgroups, int32_t iters, float* out,
                           void* stream) {
-  if (form != LSQ_PROBE_VALU_FMA && form != LSQ_PROBE_VALU_MED3 && form != LSQ_PROBE_VALU_MIXED)
-    return fail(LSQ_ERR_INVALID_ARG, "VALU probe form must be FMA, MED3 or MIXED");
+  if (form < LSQ_PROBE_VALU_FMA || form > LSQ_PROBE_VALU_MUL)
+    return fail(LSQ_ERR_INVALID_ARG, "VALU probe form must be one of lsq_probe_valu_form (0-9)");
   if (workgroups < 1 || iters < 1)
     return fail(LSQ_ERR_INVALID_ARG, "VALU probe needs at least one workgroup and one iteration");
   if (!out) return fail(LSQ_ERR_INVALID_ARG, "VALU probe output must be non-null");

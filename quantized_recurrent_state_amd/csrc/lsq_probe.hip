@@ -9,6 +9,8 @@
 // wave carries one head's packed state).
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "lsq_internal.h"
 
 namespace lsq {
@@ -132,6 +134,51 @@ __global__ __launch_bounds__(256) void valu_kernel(float* out, float x, float y,
   if (s == -1234.5f) out[0] = s;
 }
 
+// Forms 3 and up: one instruction kind each, written out in inline asm (so
+// that the compiler picks neither another encoding nor another instruction),
+// on eight independent 32-bit chains per lane, every operand a VGPR.
+template <int FORM>
+__device__ __forceinline__ uint32_t valu_op(uint32_t a, uint32_t x, uint32_t y) {
+  uint32_t d;
+  if constexpr (FORM == 3) {          // accumulating two-operand fma: d = d + x*y
+    d = a;
+    asm volatile("v_fmac_f32 %0, %1, %2" : "+v"(d) : "v"(x), "v"(y));
+  } else if constexpr (FORM == 4) {
+    asm volatile("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+                 : "=v"(d) : "v"(a), "v"(x), "v"(y));
+  } else if constexpr (FORM == 5) {
+    asm volatile("v_lshl_or_b32 %0, %1, 4, %2" : "=v"(d) : "v"(a), "v"(x));
+  } else if constexpr (FORM == 6) {
+    asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(x), "v"(y));
+  } else if constexpr (FORM == 7) {
+    asm volatile("v_xad_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(x), "v"(y));
+  } else if constexpr (FORM == 8) {
+    asm volatile("v_and_b32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(x));
+  } else {
+    asm volatile("v_mul_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(x));
+  }
+  return d;
+}
+
+template <int FORM>
+__global__ __launch_bounds__(256) void valu_asm_kernel(float* out, uint32_t x, uint32_t y, int iters) {
+  uint32_t xv = x, yv = y;
+  asm volatile("" : "+v"(xv), "+v"(yv));
+  uint32_t a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = __float_as_uint((float)(threadIdx.x + j + 1));   // normal floats
+#pragma unroll 4
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = valu_op<FORM>(a[j], xv, yv);
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s ^= a[j];
+  // never true (256-lane workgroups); the chains are kept by their volatile asm
+  if (threadIdx.x >= 256u) out[0] = __uint_as_float(s);
+}
+
 }  // namespace dev
 
 hipError_t launch_probe_valu(int form, int workgroups, int iters, float* out, hipStream_t s) {
@@ -141,7 +188,16 @@ hipError_t launch_probe_valu(int form, int workgroups, int iters, float* out, hi
   if (form == 0) hipLaunchKernelGGL((dev::valu_kernel<0>), grid, block, 0, s, out, x, y, iters);
   else if (form == 1) hipLaunchKernelGGL((dev::valu_kernel<1>), grid, block, 0, s, out, x, y, iters);
   else if (form == 2) hipLaunchKernelGGL((dev::valu_kernel<2>), grid, block, 0, s, out, x, y, iters);
-  else return hipErrorInvalidValue;
+  else {
+    uint32_t xb, yb;
+    std::memcpy(&xb, &x, 4);
+    std::memcpy(&yb, &y, 4);
+#define LSQ_VALU_ASM(F) \
+    if (form == F) hipLaunchKernelGGL((dev::valu_asm_kernel<F>), grid, block, 0, s, out, xb, yb, iters); else
+    LSQ_VALU_ASM(3) LSQ_VALU_ASM(4) LSQ_VALU_ASM(5) LSQ_VALU_ASM(6) LSQ_VALU_ASM(7) LSQ_VALU_ASM(8)
+    LSQ_VALU_ASM(9) return hipErrorInvalidValue;
+#undef LSQ_VALU_ASM
+  }
   return hipGetLastError();
 }
 

@@ -236,7 +236,7 @@ def test_probe_argument_checks_before_launch():
 
 def test_probe_valu_argument_checks_before_launch():
     L = _lib.load()
-    assert L.lsq_probe_valu(3, 1024, 8, FAKE, None) == 1      # form
+    assert L.lsq_probe_valu(10, 1024, 8, FAKE, None) == 1     # form
     assert L.lsq_probe_valu(-1, 1024, 8, FAKE, None) == 1
     assert L.lsq_probe_valu(0, 0, 8, FAKE, None) == 1         # workgroups
     assert L.lsq_probe_valu(1, 1024, 0, FAKE, None) == 1      # iterations

@@ -59,7 +59,7 @@ def test_span_walk_rewrites_every_vector(span, nt):
     assert not dst[nbytes // 4:].any()
 
 
-@pytest.mark.parametrize("form", [lsq.PROBE_VALU_FMA, lsq.PROBE_VALU_MED3, lsq.PROBE_VALU_MIXED])
+@pytest.mark.parametrize("form", list(range(10)))
 def test_valu_probe_runs_and_writes_nothing(form):
     """The chains stay finite and never hit the sentinel, so out is untouched;
     a longer run takes longer (the work is not optimised away)."""
