@@ -144,6 +144,43 @@ def test_bdr_without_update_direction(bits, dk, pol, dl, dc):
     assert rep.failed == 0 and rep.o_differ == 0, str(rep)
 
 
+def decays_near_one(d):
+    """Decays at and around the head-level bound 1 - 2^-20 of the round-up
+    candidate's range test: per head (h mod 5) exactly 1, 1 - 2^-21 (both
+    tested row by row; at 1 the bound can fail and rows take the
+    two-instruction clamp), 1 - 2^-20 (the largest decay the head-level test
+    settles), 1 - 2^-19, and the recipe's own.  A diagonal decay puts the
+    value on one column of the head and keeps the recipe's elsewhere."""
+    a = d["alpha"]
+    vals = (1.0, 1.0 - 2.0 ** -21, 1.0 - 2.0 ** -20, 1.0 - 2.0 ** -19)
+    for i, v in enumerate(vals):
+        if a.dim() == 2:
+            a[:, i::5] = v
+        else:
+            a[:, i::5, 3] = v
+
+
+NEAR1 = [(bits, dl, dc)
+         for bits in (4, 8)
+         for dl in (0, 1)
+         for dc in (lsq.DECAY_SCALAR, lsq.DECAY_DIAG)]
+
+
+@pytest.mark.parametrize("bits,dl,dc", NEAR1)
+def test_bdr_decays_near_one(bits, dl, dc):
+    """Frozen scales with directional rounding, decays at and near 1: the
+    head-level and per-row range tests of the round-up candidate, and the
+    general clamp where the test fails, all against the oracle bit for bit."""
+    group = 32 if bits == 4 else 64
+    cfg = lsq.LsqConfig(batch=2, heads=5, dk=128, dv=44, bits=bits, group=group,
+                        policy=lsq.POLICY_PERSISTENT, rounding=lsq.ROUND_BDR, delta=dl, decay=dc)
+    recipe = "gla" if dc == lsq.DECAY_DIAG else ("gdn" if dl else "mamba2")
+    rep = _run_teacher_forced(cfg, steps=6, recipe=recipe, edit=decays_near_one)
+    print(f"\n{cfg}: {rep}")
+    assert rep.ok, str(rep)
+    assert rep.failed == 0 and rep.o_differ == 0, str(rep)
+
+
 G16 = [(bits, dk, pol, rnd, dc)
        for bits in (4, 8)
        for dk in (128, 64)
