@@ -15,6 +15,10 @@ roofline    the dominant kernel (the INT4 g32 segment): its algorithmic bytes
             each launch on the launch stream, against 8 TB/s; traffic = HBM
             bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (profiles/),
             reported only while the kernel sources match the profiled ones
+valu_issue  the same launch against its arithmetic floor: its VALU instruction
+            count (profiled, same condition) per second, and the launch time
+            at full issue of its hot loop's instruction mix priced at this
+            run's VALU probe rates
 cpu_baseline  the CPU oracle on a bounded sample of the same workload (sampled
             heads, a few steps, the host threads stated), in the same unit
 
@@ -214,12 +218,14 @@ def main() -> int:
         ceiling = measure_ceiling(dev, stream, args.ceiling_gib, span_kib)
 
     traffic = None
+    valu_rec = None
     sha = kernel_source_sha()
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if (tr.get("source_sha") == sha and tr.get("workload") == wl.name
                 and tr.get("arm") == dom_a["arm"].name):
             traffic = int(tr["hbm_bytes_per_launch"])
+            valu_rec = tr.get("valu")
             # measured bytes of the other profiled segments, attached to their arms
             for a in arms:
                 a["traffic"] = traffic if a is dom_a else None
@@ -320,6 +326,7 @@ def main() -> int:
                      "frac_of_pattern_ceiling": ceiling and round(
                          dom_gbs / ceiling["span_in_place"]["gbs"], 4)},
         "ceiling": ceiling,
+        "valu_issue": valu_issue(valu_rec, ceiling, kern_ms_mean, dom_a["bytes"]),
         "fp32_state": fp32,
         "graph_replay": graph,
         "state_norms": state_norms,
@@ -327,6 +334,27 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def valu_issue(rec, ceiling, launch_ms: float, nbytes: int):
+    """The dominant launch against its arithmetic floor: its VALU instruction
+    count (from the profile of the same kernel sources) over the launch time,
+    and the launch time at full issue of its hot loop's instruction mix priced
+    at this run's probe rates (kinds without a probe form at the med3 rate)."""
+    if not rec or not ceiling or "valu" not in ceiling:
+        return None
+    rates = {k: v["wave_instr_per_s"] for k, v in ceiling["valu"].items()}
+    loop = rec["hot_loop_per_row_iteration"]
+    per_row = sum(n / rates.get(k, rates["med3"]) for k, n in loop.items())
+    rows = rec["waves_per_launch"] * rec["row_iterations_per_wave"]
+    floor_s = rows * per_row + rec["waves_per_launch"] * rec["setup_per_wave"] / rates["med3"]
+    t = launch_ms * 1e-3
+    return {"instr_per_launch": rec["instr_per_launch"],
+            "achieved_wave_instr_per_s": round(rec["instr_per_launch"] / t / 1e9, 2) * 1e9,
+            "fmac_probe_wave_instr_per_s": rates.get("fmac"),
+            "priced_floor_us": round(floor_s * 1e6, 1),
+            "frac_of_priced_floor": round(floor_s / t, 4),
+            "hbm_frac_at_floor": round(nbytes / floor_s / (PEAK_HBM_GBS * 1e9), 4)}
 
 
 def measure_ceiling(dev, stream, gib: float, span_kib: int) -> dict:
