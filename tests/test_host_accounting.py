@@ -40,3 +40,25 @@ def test_prefill_bytes_scalar_decay_persistent():
                         policy=lsq.POLICY_PERSISTENT)
     per_head = 4 * 100 * (64 + 128 + 1 + 1) + 2 * 128 * 64 + 128 * 2 * 4
     assert runner.prefill_algorithmic_bytes(cfg, 100) == 2 * per_head
+
+
+def test_valu_issue_prices_the_hot_loop_at_the_probe_rates():
+    """bench.valu_issue: one row-iteration's instructions, each at its probe
+    rate (unlisted kinds at the med3 rate), times the rows, plus the set-up at
+    the med3 rate; a hand count for a two-kind histogram."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    rec = {"instr_per_launch": 3.0e9, "waves_per_launch": 10, "row_iterations_per_wave": 4,
+           "hot_loop_per_row_iteration": {"fma": 60, "other": 10}, "setup_per_wave": 20}
+    ceiling = {"valu": {"fma": {"wave_instr_per_s": 1.0e6}, "med3": {"wave_instr_per_s": 0.5e6},
+                        "fmac": {"wave_instr_per_s": 2.0e6}}}
+    got = bench.valu_issue(rec, ceiling, launch_ms=2.0, nbytes=8_000_000)
+    floor = 40 * (60 / 1.0e6 + 10 / 0.5e6) + 10 * 20 / 0.5e6      # seconds: 0.0032 + 0.0004
+    assert abs(got["priced_floor_us"] - floor * 1e6) < 0.05
+    assert abs(got["frac_of_priced_floor"] - floor / 2.0e-3) < 1e-4
+    assert abs(got["achieved_wave_instr_per_s"] - 3.0e9 / 2.0e-3) < 1e7
+    assert abs(got["hbm_frac_at_floor"] - 8_000_000 / floor / 8.0e12) < 1e-4
+    assert bench.valu_issue(rec, None, 2.0, 1) is None
+    assert bench.valu_issue(None, ceiling, 2.0, 1) is None
